@@ -1,0 +1,105 @@
+// C ABI of libhybridattn.so (declared in include/hybrid_attn.h): host-side
+// argument checks, workspace sizing, then the launches on the caller's stream.
+#include "hybrid_attn.h"
+#include "ha_common.hpp"
+#include "ha_internal.hpp"
+
+namespace {
+
+bool supported_shape(int head_dim, int page_size, ha_dtype dtype) {
+  return (head_dim == 64 || head_dim == 128) && page_size == ha::kPage &&
+         (dtype == HA_DTYPE_F32 || dtype == HA_DTYPE_BF16);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ha_status_string(ha_status status) {
+  switch (status) {
+    case HA_OK: return "HA_OK";
+    case HA_ERR_INVALID_ARGUMENT: return "HA_ERR_INVALID_ARGUMENT";
+    case HA_ERR_UNSUPPORTED: return "HA_ERR_UNSUPPORTED";
+    case HA_ERR_WORKSPACE_TOO_SMALL: return "HA_ERR_WORKSPACE_TOO_SMALL";
+    case HA_ERR_HIP: return "HA_ERR_HIP";
+  }
+  return "HA_ERR_UNKNOWN";
+}
+
+ha_status paged_kv_append(const void* key, const void* value, const int32_t* slot_mapping,
+                          void* k_cache, void* v_cache, int32_t total_tokens,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                          int32_t num_blocks, ha_dtype dtype, void* stream) {
+  if (total_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || page_size <= 0 ||
+      num_blocks <= 0)
+    return HA_ERR_INVALID_ARGUMENT;
+  if (!supported_shape(head_dim, page_size, dtype)) return HA_ERR_UNSUPPORTED;
+  if (!k_cache || !v_cache) return HA_ERR_INVALID_ARGUMENT;
+  if (total_tokens == 0) return HA_OK;
+  if (!key || !value || !slot_mapping) return HA_ERR_INVALID_ARGUMENT;
+  if (static_cast<long long>(num_blocks) * page_size > 0x7fffffffLL) return HA_ERR_INVALID_ARGUMENT;
+  hipError_t e = ha::launch_kv_append(key, value, slot_mapping, k_cache, v_cache, total_tokens,
+                                      num_kv_heads, head_dim, num_blocks,
+                                      dtype == HA_DTYPE_F32 ? 0 : 1,
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? HA_OK : HA_ERR_HIP;
+}
+
+size_t hybrid_attn_workspace_size(int32_t num_seqs, int32_t total_q, int32_t max_seqlen_k,
+                                  int32_t num_heads, int32_t head_dim) {
+  (void)total_q;
+  if (num_seqs < 1 || max_seqlen_k < 0 || num_heads < 1 || head_dim < 1) return 0;
+  return ha::ws_layout(num_seqs, max_seqlen_k, num_heads, head_dim).total;
+}
+
+ha_status hybrid_attn_fwd(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                          const int32_t* block_table, void* out, int32_t num_seqs,
+                          int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t page_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                          float sm_scale, ha_dtype dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (num_seqs < 1 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_heads < 1 ||
+      num_kv_heads < 1 || head_dim < 1 || page_size < 1 || num_blocks < 1 ||
+      max_blocks_per_seq < 1)
+    return HA_ERR_INVALID_ARGUMENT;
+  if (num_heads % num_kv_heads != 0 || max_seqlen_q > max_seqlen_k ||
+      max_seqlen_k > ha::kMaxSeqlenK)
+    return HA_ERR_INVALID_ARGUMENT;
+  if (static_cast<long long>(num_blocks) * page_size > 0x7fffffffLL) return HA_ERR_INVALID_ARGUMENT;
+  if (!supported_shape(head_dim, page_size, dtype)) return HA_ERR_UNSUPPORTED;
+  if (!cu_seqlens_q || !seqlens_k || !block_table || !k_cache || !v_cache || !workspace)
+    return HA_ERR_INVALID_ARGUMENT;
+  if (total_q > 0 && (!q || !out)) return HA_ERR_INVALID_ARGUMENT;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return HA_ERR_INVALID_ARGUMENT;
+  const ha::WsLayout ws = ha::ws_layout(num_seqs, max_seqlen_k, num_heads, head_dim);
+  if (workspace_bytes < ws.total) return HA_ERR_WORKSPACE_TOO_SMALL;
+  if (total_q == 0) return HA_OK;
+
+  ha::AttnLaunch L;
+  L.q = q;
+  L.k_cache = k_cache;
+  L.v_cache = v_cache;
+  L.cu_seqlens_q = cu_seqlens_q;
+  L.seqlens_k = seqlens_k;
+  L.block_table = block_table;
+  L.out = out;
+  L.num_seqs = num_seqs;
+  L.total_q = total_q;
+  L.max_seqlen_q = max_seqlen_q;
+  L.max_seqlen_k = max_seqlen_k;
+  L.num_heads = num_heads;
+  L.num_kv_heads = num_kv_heads;
+  L.head_dim = head_dim;
+  L.num_blocks = num_blocks;
+  L.max_blocks = max_blocks_per_seq;
+  L.sm_scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf(static_cast<float>(head_dim));
+  L.dtype = dtype == HA_DTYPE_F32 ? 0 : 1;
+  L.workspace = static_cast<unsigned char*>(workspace);
+  L.ws = ws;
+  L.stream = static_cast<hipStream_t>(stream);
+  return ha::launch_attention(L) == hipSuccess ? HA_OK : HA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Host/device contract between the C-ABI layer (api.hip) and the kernel files
+// (kv_append.hip, attention.hip): workspace layout, tuning constants and the
+// launcher entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ha {
+
+// ---- tuning constants (gfx950) ---------------------------------------------------
+constexpr int kThreads = 256;       // 4 waves per workgroup for every kernel role
+constexpr int kChunkRows = 128;     // query rows per chunk tile (32 per wave)
+constexpr int kSplitMin = 256;      // smallest decode KV split, in keys
+constexpr int kSplitCandidates = 23;  // decode split sizes kSplitMin << k, k < 23 (up to 2^30)
+constexpr int kPartsMax = 16384;    // cap on (segment, split) partial slots
+constexpr int kItemsPerSlot = 8;    // decode work items aimed at per resident workgroup
+constexpr int kHeadsPerDecodeItem = 4;  // one head per wave
+constexpr int kMaxSeqlenK = 1 << 30;
+
+// ---- workspace ---------------------------------------------------------------------
+// [header 256 B][chunk_prefix (B+1)][dec_prefix (B+1)][part_prefix (B+1)]
+// [partials parts_cap x H x (D + 4) fp32]; every array starts on a 256-byte boundary.
+struct PlanHeader {
+  uint32_t counter;       // next work item (reset to 0 by the planner each call)
+  int32_t n_chunk_items;  // items [0, n_chunk_items) are chunk tiles
+  int32_t n_dec_items;    // items [n_chunk_items, +n_dec_items) are decode splits
+  int32_t split;          // decode split size in keys (multiple of 64)
+  int32_t n_parts;        // partial slots in use
+  int32_t bad_segments;   // segments skipped because they broke a precondition
+  int32_t pad[58];
+};
+static_assert(sizeof(PlanHeader) == 256, "header is 256 bytes");
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct WsLayout {
+  size_t chunk_prefix, dec_prefix, part_prefix, partials, total;
+  int parts_cap;
+  int part_stride;  // floats per (part, head): m, l, 2 pad, acc[D]
+};
+
+inline int parts_cap_for(int num_seqs, int max_seqlen_k) {
+  long long per_seq = (static_cast<long long>(max_seqlen_k) + kSplitMin - 1) / kSplitMin;
+  long long cap = static_cast<long long>(num_seqs) * per_seq;
+  return static_cast<int>(cap < kPartsMax ? cap : kPartsMax);
+}
+
+inline WsLayout ws_layout(int num_seqs, int max_seqlen_k, int num_heads, int head_dim) {
+  WsLayout l;
+  size_t off = sizeof(PlanHeader);
+  size_t arr = align256(sizeof(int32_t) * (static_cast<size_t>(num_seqs) + 1));
+  l.chunk_prefix = off; off += arr;
+  l.dec_prefix = off; off += arr;
+  l.part_prefix = off; off += arr;
+  l.parts_cap = parts_cap_for(num_seqs, max_seqlen_k);
+  l.part_stride = head_dim + 4;
+  l.partials = off;
+  off += align256(sizeof(float) * static_cast<size_t>(l.parts_cap) * num_heads * l.part_stride);
+  l.total = off;
+  return l;
+}
+
+// ---- launchers ---------------------------------------------------------------------
+struct AttnLaunch {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* cu_seqlens_q;
+  const int32_t* seqlens_k;
+  const int32_t* block_table;
+  void* out;
+  int num_seqs, total_q, max_seqlen_q, max_seqlen_k;
+  int num_heads, num_kv_heads, head_dim, num_blocks, max_blocks;
+  float sm_scale;
+  int dtype;  // 0 = f32, 1 = bf16
+  unsigned char* workspace;
+  WsLayout ws;
+  hipStream_t stream;
+};
+
+hipError_t launch_kv_append(const void* key, const void* value, const int32_t* slot_mapping,
+                            void* k_cache, void* v_cache, int total_tokens, int num_kv_heads,
+                            int head_dim, int num_blocks, int dtype, hipStream_t stream);
+
+hipError_t launch_attention(const AttnLaunch& a);
+
+}  // namespace ha

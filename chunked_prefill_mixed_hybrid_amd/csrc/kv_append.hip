@@ -1,0 +1,50 @@
+// paged_kv_append: copy each new token's K and V rows into the page slot its
+// slot_mapping entry names.  A token row of one pool is [Hkv, D] contiguous
+// both in key/value [T, Hkv, D] and in the cache [NB, P, Hkv, D] (slot s starts
+// at element s * Hkv * D), so the append is a gather-free scatter of
+// contiguous rows, done with 16-byte vector loads and stores.
+// Sources: wangyu.me Chunked Prefill page, section "输入组装" (slot_mapping
+// write before attention); lpnh.cn FlashInfer article, section 4.2 (append
+// through the page table).  Slots are distinct by precondition, so no atomics.
+#include "ha_common.hpp"
+#include "ha_internal.hpp"
+
+namespace ha {
+
+// One thread moves one 16-byte chunk of K and the same chunk of V.
+// grid.x * blockDim.x >= total_tokens * chunks_per_row (checked by the launcher).
+__global__ __launch_bounds__(kThreads) void kv_append_kernel(
+    const u32x4_t* __restrict__ key, const u32x4_t* __restrict__ value,
+    const int32_t* __restrict__ slot_mapping, u32x4_t* __restrict__ k_cache,
+    u32x4_t* __restrict__ v_cache, int total_tokens, int chunks_per_row, long long pool_slots) {
+  const long long idx = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x;
+  const long long total = static_cast<long long>(total_tokens) * chunks_per_row;
+  if (idx >= total) return;
+  const int t = static_cast<int>(idx / chunks_per_row);
+  const int c = static_cast<int>(idx - static_cast<long long>(t) * chunks_per_row);
+  const int slot = slot_mapping[t];
+  if (slot < 0 || slot >= pool_slots) return;  // padding token or slot outside the pool
+  const size_t dst = static_cast<size_t>(slot) * chunks_per_row + c;
+  k_cache[dst] = key[idx];
+  v_cache[dst] = value[idx];
+}
+
+hipError_t launch_kv_append(const void* key, const void* value, const int32_t* slot_mapping,
+                            void* k_cache, void* v_cache, int total_tokens, int num_kv_heads,
+                            int head_dim, int num_blocks, int dtype, hipStream_t stream) {
+  const int elem_bytes = dtype == 0 ? 4 : 2;
+  const long long row_bytes = static_cast<long long>(num_kv_heads) * head_dim * elem_bytes;
+  const int chunks_per_row = static_cast<int>(row_bytes / 16);  // head_dim * elem_bytes % 16 == 0
+  const long long total = static_cast<long long>(total_tokens) * chunks_per_row;
+  if (total == 0) return hipSuccess;
+  const long long blocks = (total + kThreads - 1) / kThreads;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kv_append_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                     stream, static_cast<const u32x4_t*>(key), static_cast<const u32x4_t*>(value),
+                     slot_mapping, static_cast<u32x4_t*>(k_cache), static_cast<u32x4_t*>(v_cache),
+                     total_tokens, chunks_per_row,
+                     static_cast<long long>(num_blocks) * kPage);
+  return hipGetLastError();
+}
+
+}  // namespace ha

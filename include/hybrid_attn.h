@@ -1,0 +1,147 @@
+/*
+ * hybrid_attn.h -- C ABI of libhybridattn.so: one mixed chunked-prefill step
+ * of paged attention on an AMD Instinct MI355X (gfx950).
+ *
+ * A step packs ragged query segments -- decode segments of one token and
+ * prefill chunks of many -- into one tensor, and every segment attends only to
+ * its own KV history, which lives in fixed-size pages located through a
+ * per-request block table.  Sources for what is computed:
+ *   [VARLEN]  "大语言模型推理优化（二）：Chunked Prefill" (wangyu.me), sections
+ *             "记录 KV Cache 的长度" and "Flash Attention 的 varlen 接口":
+ *             cu_seqlens_q packing, segment isolation, causal mask with the
+ *             query segment aligned to the END of its KV segment, decode =
+ *             query length 1.
+ *   [ORDER]   same page, section "在 vLLM 中是如何实现的 / 输入组装": the new
+ *             K/V are written through slot_mapping into the paged cache first,
+ *             then the varlen paged kernel gathers history via block_table.
+ *   [PAGED]   kwkr.cn Triton hybrid-attention article, kernel section: page
+ *             = block_table[pos / PAGE_SIZE], offset = pos % PAGE_SIZE,
+ *             scale = 1/sqrt(head_dim), online softmax in fp32.
+ *   [APPEND]  "技术融合剖析：Chunked Prefill如何借助FlashAttention/FlashInfer实现
+ *             混合批次推理" (lpnh.cn), section 4.2: the append translates each
+ *             new token through the block table and writes it into its page.
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense and row-major in the layouts given below; pointers
+ *     marked "device" are HIP device pointers, the rest are host values.
+ *   - The caller allocates and owns every buffer, the workspace included.  The
+ *     library keeps no pointer after a call returns, allocates no device
+ *     memory, and never synchronises: work is enqueued on `stream` (a
+ *     hipStream_t; NULL = the default stream) and the call returns at once.
+ *   - No exception crosses the ABI.  Host-checkable argument problems are
+ *     reported before anything is enqueued.  HA_ERR_HIP reports a failed
+ *     launch (hipGetLastError after the launch).
+ *   - Device-resident metadata is trusted for performance but never able to
+ *     make a kernel read or write outside the buffers: segments that break a
+ *     precondition (Lq > Lk, Lk > max_seqlen_k, Lq > max_seqlen_q, more pages
+ *     than max_blocks_per_seq, cu_seqlens_q not non-decreasing or past
+ *     total_q) are skipped and their output rows are left unwritten; block ids
+ *     outside [0, num_blocks) read as zero rows; slots outside the pool are
+ *     skipped by the append.
+ *   - Supported: dtype F32 or BF16 (output = input dtype, fp32 -> bf16 by
+ *     round-to-nearest-even), head_dim 64 or 128, page_size 16,
+ *     num_heads % num_kv_heads == 0 (query head h reads KV head
+ *     h / (num_heads / num_kv_heads)).
+ */
+#ifndef HYBRID_ATTN_H
+#define HYBRID_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HA_OK = 0,
+  HA_ERR_INVALID_ARGUMENT = 1, /* null pointer, non-positive size, bad head ratio, ... */
+  HA_ERR_UNSUPPORTED = 2,      /* dtype, head_dim or page_size outside the supported set */
+  HA_ERR_WORKSPACE_TOO_SMALL = 3,
+  HA_ERR_HIP = 4 /* a HIP runtime call or kernel launch failed */
+} ha_status;
+
+typedef enum { HA_DTYPE_F32 = 0, HA_DTYPE_BF16 = 1 } ha_dtype;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* ha_status_string(ha_status status);
+
+/*
+ * paged_kv_append -- write this step's new keys/values into the paged pools
+ * [ORDER][APPEND].  Call it BEFORE hybrid_attn_fwd for the same step, on the
+ * same stream, so that seqlens_k can include the new tokens.
+ *
+ *   key, value    device [total_tokens, num_kv_heads, head_dim], dtype
+ *   slot_mapping  device int32 [total_tokens]; token t goes to page
+ *                 slot / page_size, offset slot % page_size.  A negative slot
+ *                 skips the token (padding).  Slots must be distinct; two
+ *                 tokens naming one slot leave either token's row there.
+ *   k_cache, v_cache  device [num_blocks, page_size, num_kv_heads, head_dim]
+ *
+ * The copy is bit-exact; no other byte of either pool is written.
+ * Returns HA_ERR_INVALID_ARGUMENT for null pointers or non-positive sizes
+ * (total_tokens == 0 is a valid no-op), HA_ERR_UNSUPPORTED for other dtypes,
+ * head_dim or page_size.
+ */
+ha_status paged_kv_append(const void* key, const void* value, const int32_t* slot_mapping,
+                          void* k_cache, void* v_cache, int32_t total_tokens,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                          int32_t num_blocks, ha_dtype dtype, void* stream);
+
+/*
+ * hybrid_attn_workspace_size -- bytes of device workspace hybrid_attn_fwd
+ * needs for a step with these bounds (plan arrays, work counter and split-KV
+ * partial results).  Depends only on host-known bounds.
+ */
+size_t hybrid_attn_workspace_size(int32_t num_seqs, int32_t total_q, int32_t max_seqlen_k,
+                                  int32_t num_heads, int32_t head_dim);
+
+/*
+ * hybrid_attn_fwd -- one fused varlen paged attention forward for a mixed
+ * step, causal with right alignment [VARLEN][PAGED].
+ *
+ * For segment b with Lq = cu_seqlens_q[b+1] - cu_seqlens_q[b] and
+ * Lk = seqlens_k[b] (history plus this step's new tokens), query row i
+ * (packed row r = cu_seqlens_q[b] + i) of head h sees the keys at positions
+ * 0 .. (Lk - Lq) + i of its own segment, and
+ *   out[r, h, :] = sum_j softmax_j(sm_scale * <q[r, h, :], K_j>) * V_j
+ * where K_j / V_j are read from page block_table[b][j / page_size], offset
+ * j % page_size, KV head h / (num_heads / num_kv_heads).
+ *
+ *   q             device [total_q, num_heads, head_dim], dtype
+ *   k_cache, v_cache  device [num_blocks, page_size, num_kv_heads, head_dim]
+ *   cu_seqlens_q  device int32 [num_seqs + 1], cu_seqlens_q[0] = 0, non-decreasing,
+ *                 cu_seqlens_q[num_seqs] = total_q
+ *   seqlens_k     device int32 [num_seqs], 0 <= Lq_b <= Lk_b <= max_seqlen_k
+ *   block_table   device int32 [num_seqs, max_blocks_per_seq]; the first
+ *                 ceil(Lk_b / page_size) entries of row b are physical block
+ *                 ids in [0, num_blocks); later entries are never read
+ *   out           device [total_q, num_heads, head_dim], dtype; rows of
+ *                 segments with Lq = 0 do not exist, every other row is written
+ *   max_seqlen_q, max_seqlen_k  host upper bounds of Lq_b and Lk_b
+ *   sm_scale      softmax scale (1/sqrt(head_dim) on the pages); values <= 0
+ *                 select 1/sqrt(head_dim)
+ *   workspace     device, at least hybrid_attn_workspace_size(...) bytes,
+ *                 256-byte aligned; its content on entry does not matter.  It
+ *                 is in use until the enqueued work finishes: calls that share
+ *                 a workspace must be ordered (e.g. on one stream).
+ *
+ * Errors: HA_ERR_INVALID_ARGUMENT (null pointers, num_seqs < 1, total_q < 0,
+ * num_heads % num_kv_heads != 0, max_seqlen_q > max_seqlen_k, non-positive
+ * sizes), HA_ERR_UNSUPPORTED (dtype, head_dim, page_size),
+ * HA_ERR_WORKSPACE_TOO_SMALL, HA_ERR_HIP.
+ */
+ha_status hybrid_attn_fwd(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                          const int32_t* block_table, void* out, int32_t num_seqs,
+                          int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t page_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                          float sm_scale, ha_dtype dtype, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYBRID_ATTN_H */

@@ -1,0 +1,132 @@
+"""Helpers of the GPU parity tests: run the HIP path through the C ABI, run the
+oracle on the same bytes, compare at the stated tolerances."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+from chunked_prefill_mixed_hybrid_amd import binding as B
+from chunked_prefill_mixed_hybrid_amd import workload as W
+import oracle as O
+
+# Tolerances: fp32 max |err| <= 1e-4; bf16 max |err| <= 2e-2 AND
+# ||err||_2 / ||ref||_2 <= 1e-2 (both must hold); any NaN/Inf fails.
+TOL_F32_ABS = 1e-4
+TOL_BF16_ABS = 2e-2
+TOL_BF16_REL = 1e-2
+
+
+def note(msg: str) -> None:
+    """Progress line that bypasses pytest capture (names the GPU case first)."""
+    sys.__stderr__.write(f"[gpu] {msg}\n")
+    sys.__stderr__.flush()
+
+
+def require_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU test run without a GPU")
+    B.load()
+
+
+def gpu_step(ds: W.DeviceStep, workspace=None, append=True):
+    """paged_kv_append then hybrid_attn_fwd, exactly as a step runs them."""
+    import torch
+    m = ds.meta
+    if append:
+        B.paged_kv_append(ds.key, ds.value, ds.slot_mapping, ds.k_cache, ds.v_cache)
+    out = torch.empty_like(ds.q)
+    B.hybrid_attn_fwd(ds.q, ds.k_cache, ds.v_cache, ds.cu_seqlens_q, ds.seqlens_k,
+                      ds.block_table, m.max_seqlen_q, m.max_seqlen_k, out=out,
+                      workspace=workspace)
+    torch.cuda.synchronize()
+    return out
+
+
+def to_f64(t) -> np.ndarray:
+    return O.to_f64(W.to_host_array(t))
+
+
+def compare(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "") -> dict:
+    """got, ref: float64 arrays of the same shape."""
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = got - ref
+    max_abs = float(np.max(np.abs(err))) if err.size else 0.0
+    nref = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(err) / nref) if nref > 0 else 0.0
+    stats = {"max_abs": max_abs, "rel_norm": rel}
+    if dtype == W.F32:
+        assert max_abs <= TOL_F32_ABS, f"{what}: fp32 max abs err {max_abs}"
+    else:
+        assert max_abs <= TOL_BF16_ABS, f"{what}: bf16 max abs err {max_abs}"
+        assert rel <= TOL_BF16_REL, f"{what}: bf16 rel norm err {rel}"
+    return stats
+
+
+def host_pools(ds: W.DeviceStep):
+    return W.to_host_array(ds.k_cache), W.to_host_array(ds.v_cache)
+
+
+def oracle_full(ds: W.DeviceStep, kc_host, vc_host, row_select=None):
+    """Oracle append + attention on host copies of the PRE-append pools."""
+    orc = O.default()
+    m = ds.meta
+    kc, vc = kc_host.copy(), vc_host.copy()
+    orc.append(W.to_host_array(ds.key), W.to_host_array(ds.value), m.slot_mapping, kc, vc)
+    out = orc.attention(W.to_host_array(ds.q), kc, vc, m.cu_seqlens_q, m.seqlens_k,
+                        m.block_table, row_select=row_select)
+    return out, kc, vc
+
+
+class SampledStep:
+    """Pages, rows and metadata of a few segments of a big step, copied to the
+    host BEFORE the GPU append, with block ids renumbered compactly, so the
+    oracle can check those segments (and their append) on its own."""
+
+    def __init__(self, ds: W.DeviceStep, segs):
+        import torch
+        m = ds.meta
+        p = m.page_size
+        self.segs = list(segs)
+        pages, rows, lqs, lks = [], [], [], []
+        for b in self.segs:
+            lk = int(m.seqlens_k[b])
+            r0, r1 = int(m.cu_seqlens_q[b]), int(m.cu_seqlens_q[b + 1])
+            n = (lk + p - 1) // p
+            pages.append(m.block_table[b, :n].astype(np.int64))
+            rows.append(np.arange(r0, r1))
+            lqs.append(r1 - r0)
+            lks.append(lk)
+        allp = np.concatenate(pages)
+        self.pages = allp
+        self.rows = np.concatenate(rows)
+        remap = {int(pg): i for i, pg in enumerate(allp)}
+        mb = max(len(x) for x in pages)
+        bt = np.full((len(self.segs), mb), -1, np.int32)
+        off = 0
+        for i, x in enumerate(pages):
+            bt[i, :len(x)] = np.arange(off, off + len(x))
+            off += len(x)
+        self.block_table = bt
+        self.cu = np.concatenate([[0], np.cumsum(lqs)]).astype(np.int32)
+        self.sk = np.array(lks, np.int32)
+        slots = m.slot_mapping[self.rows].astype(np.int64)
+        self.slot_mapping = np.array([remap[int(s) // p] * p + int(s) % p for s in slots], np.int32)
+        idx = torch.from_numpy(allp).to(ds.k_cache.device)
+        self.kc = W.to_host_array(ds.k_cache.index_select(0, idx))
+        self.vc = W.to_host_array(ds.v_cache.index_select(0, idx))
+        ridx = torch.from_numpy(self.rows).to(ds.q.device)
+        self.q = W.to_host_array(ds.q.index_select(0, ridx))
+        self.key = W.to_host_array(ds.key.index_select(0, ridx))
+        self.value = W.to_host_array(ds.value.index_select(0, ridx))
+        self.page_idx = idx
+
+    def oracle(self, row_select=None):
+        orc = O.default()
+        kc, vc = self.kc.copy(), self.vc.copy()
+        orc.append(self.key, self.value, self.slot_mapping, kc, vc)
+        out = orc.attention(self.q, kc, vc, self.cu, self.sk, self.block_table,
+                            row_select=row_select)
+        return out, kc, vc

@@ -1,0 +1,254 @@
+"""HIP path (through the C ABI) against the CPU oracle, element by element.
+
+KV append: bit-exact.  Attention: fp32 max |err| <= 1e-4; bf16 max |err| <=
+2e-2 and relative L2 error <= 1e-2.  Inputs are seeded and synthetic with the
+shapes of the five workload configs plus a sweep of small ragged shapes; cache
+slots no kernel may read (tails of last pages, spare pages, new-token slots
+before the append) hold NaN.
+"""
+import numpy as np
+import pytest
+
+from chunked_prefill_mixed_hybrid_amd import binding as B
+from chunked_prefill_mixed_hybrid_amd import workload as W
+import gpu_support as G
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    G.require_gpu()
+    yield
+    import torch
+    torch.cuda.empty_cache()
+
+
+def _free():
+    import gc
+    import torch
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- small sweep
+SWEEP = [
+    # (segments (Lq, Lk), Hq, Hkv, D, dtype, seed)
+    ([(1, 1), (1, 17), (1, 300), (1, 64), (1, 65)], 4, 4, 128, W.BF16, 1),
+    ([(130, 130)], 2, 2, 128, W.BF16, 2),
+    ([(200, 1000)], 2, 2, 128, W.BF16, 3),
+    ([(1, 500), (129, 700), (1, 33), (2, 2), (17, 40)], 4, 4, 64, W.BF16, 4),
+    ([(1, 500), (129, 700), (1, 33), (2, 2), (17, 40)], 3, 3, 64, W.F32, 5),
+    ([(1, 77), (100, 333), (1, 1)], 2, 2, 128, W.F32, 6),
+    ([(1, 900), (70, 300), (1, 2)], 8, 2, 128, W.BF16, 7),
+    ([(0, 5), (3, 10), (1, 7), (0, 0)], 4, 4, 128, W.BF16, 8),
+    ([(1, 5000), (1, 3000), (64, 64)], 4, 4, 128, W.BF16, 9),
+    ([(128, 128), (256, 1024), (1, 1024)], 4, 4, 128, W.BF16, 10),
+    ([(1, 4097), (33, 4129)], 64, 64, 128, W.BF16, 11),
+    ([(5, 5), (1, 2000), (300, 2300)], 2, 1, 64, W.F32, 12),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SWEEP)))
+def test_small_sweep(case):
+    segs, hq, hkv, d, dt, seed = SWEEP[case]
+    spec, meta = W.custom_step(segs, hq, hkv, d, dt, seed=seed)
+    hs = W.host_values(spec, meta, seed=seed)
+    ds = _dev(hs)
+    ref, kc_ref, vc_ref = G.oracle_full(ds, hs.k_cache, hs.v_cache)
+    G.note(f"small_sweep case={case} segs={segs} H={hq}/{hkv} D={d} {dt}")
+    out = G.gpu_step(ds)
+    kc, vc = G.host_pools(ds)
+    assert kc.tobytes() == kc_ref.tobytes() and vc.tobytes() == vc_ref.tobytes()
+    G.compare(G.to_f64(out), ref, dt, f"sweep case {case}")
+
+
+def _dev(hs):
+    return W.to_device(hs, "cuda")
+
+
+# ---------------------------------------------------------------- full configs
+def test_config1_worked_example():
+    spec, meta = W.make_step(1)
+    hs = W.host_values(spec, meta, seed=0)
+    ds = _dev(hs)
+    ref, kc_ref, vc_ref = G.oracle_full(ds, hs.k_cache, hs.v_cache)
+    G.note("config1 worked example fp32 H=2 D=64")
+    out = G.gpu_step(ds)
+    kc, vc = G.host_pools(ds)
+    assert kc.tobytes() == kc_ref.tobytes() and vc.tobytes() == vc_ref.tobytes()
+    G.compare(G.to_f64(out), ref, W.F32, "config 1")
+
+
+def test_config2_full():
+    spec, meta = W.make_step(2)
+    ds = W.device_values(spec, meta, seed=0)
+    kc0, vc0 = G.host_pools(ds)
+    ref, kc_ref, vc_ref = G.oracle_full(ds, kc0, vc0)
+    del kc0, vc0
+    G.note("config2 2x512 chunks + 30 decodes bf16 H=32 D=128")
+    out = G.gpu_step(ds)
+    kc, vc = G.host_pools(ds)
+    assert kc.tobytes() == kc_ref.tobytes() and vc.tobytes() == vc_ref.tobytes()
+    G.compare(G.to_f64(out), ref, W.BF16, "config 2")
+    del ds
+    _free()
+
+
+def _sampled_config(config, n_random_dec, chunk_rows, seed=0):
+    import torch
+    spec, meta = W.make_step(config)
+    ds = W.device_values(spec, meta, seed=0)
+    lq = np.diff(meta.cu_seqlens_q)
+    dec = np.flatnonzero(lq == 1)
+    chunk = np.flatnonzero(lq > 1)
+    rng = np.random.default_rng(100 + config)
+    pick = set(rng.choice(dec, size=min(n_random_dec, len(dec)), replace=False).tolist())
+    pick |= {int(dec[np.argmax(meta.seqlens_k[dec])]), int(dec[np.argmin(meta.seqlens_k[dec])])}
+    segs = sorted(pick | set(chunk.tolist()))
+    smp = G.SampledStep(ds, segs)
+    sel = np.zeros(len(smp.rows), np.uint8)
+    local = 0
+    for b in segs:
+        n = int(lq[b])
+        if n == 1:
+            sel[local] = 1
+        else:
+            for r in chunk_rows(n, rng):
+                sel[local + r] = 1
+        local += n
+    # device-side copies of the pools: after the append, every slot other than
+    # this step's new-token slots must be bitwise unchanged
+    k_before, v_before = ds.k_cache.clone(), ds.v_cache.clone()
+    G.note(f"config{config} sampled: {len(segs)} segments, {int(sel.sum())} rows")
+    out = G.gpu_step(ds)
+    hkv, d = spec.num_kv_heads, spec.head_dim
+    slots = ds.slot_mapping.long()
+    for before, after, new in ((k_before, ds.k_cache, ds.key), (v_before, ds.v_cache, ds.value)):
+        a16 = after.view(-1, hkv * d).view(torch.int16)
+        assert torch.equal(a16.index_select(0, slots), new.reshape(-1, hkv * d).view(torch.int16))
+        before.view(-1, hkv * d).index_copy_(0, slots, new.reshape(-1, hkv * d))
+        assert torch.equal(before.view(torch.int16), after.view(torch.int16))
+    del k_before, v_before
+    ref, kc_ref, vc_ref = smp.oracle(row_select=sel)
+    # append of the sampled segments, bit-exact against the oracle
+    kc_got = W.to_host_array(ds.k_cache.index_select(0, smp.page_idx))
+    vc_got = W.to_host_array(ds.v_cache.index_select(0, smp.page_idx))
+    assert kc_got.tobytes() == kc_ref.tobytes() and vc_got.tobytes() == vc_ref.tobytes()
+    import torch as _t
+    got = G.to_f64(out.index_select(0, _t.from_numpy(smp.rows).to(out.device)))
+    rows = sel.astype(bool)
+    stats = G.compare(got[rows], ref[rows], W.BF16, f"config {config} sampled")
+    del ds, out
+    _free()
+    return stats
+
+
+def _edge_rows(n, rng, extra=6):
+    base = {0, 1, n - 1, n // 2}
+    for t in range(128, n, 128):
+        base |= {t - 1, t}
+    base = {r for r in base if 0 <= r < n}
+    base |= set(rng.choice(n, size=min(extra, n), replace=False).tolist())
+    return sorted(base)
+
+
+def test_config3_sampled():
+    _sampled_config(3, 12, _edge_rows)
+
+
+def test_config4_sampled():
+    _sampled_config(4, 3, lambda n, rng: sorted({0, 1, 127, 128, 511, 512, n - 1} |
+                                                 set(rng.choice(n, 3, replace=False).tolist())))
+
+
+def test_config5_sampled():
+    _sampled_config(5, 12, lambda n, rng: sorted({0, 1, 127, 128, 1023, 1024, n - 1} |
+                                                 set(rng.choice(n, 25, replace=False).tolist())))
+
+
+# ---------------------------------------------------------------- chunk invariance
+def test_chunk_invariance_10000_prompt():
+    """The 10000-token prompt prefilled as 4 x 2048 + 1808 gives the same KV
+    bytes as one full prefill and outputs within tolerance of it and of the
+    oracle (H=64, D=128, bf16, as in the budget-2048 workload)."""
+    import torch
+    steps = W.chunked_prompt_steps(10000, 2048)
+    spec, meta = W.custom_step([(10000, 10000)], 64, 64, 128, W.BF16, seed=21)
+    full = W.device_values(spec, meta, seed=21)
+    k0, v0 = full.k_cache.clone(), full.v_cache.clone()
+    kc_host, vc_host = G.host_pools(full)
+    G.note("chunk invariance: full 10000-token prefill")
+    out_full = G.gpu_step(full)
+    outs = []
+    for lq, lk in steps:
+        h0 = lk - lq
+        ds = W.DeviceStep(spec, meta, full.q[h0:lk], full.key[h0:lk], full.value[h0:lk], k0, v0,
+                          torch.tensor([0, lq], dtype=torch.int32, device="cuda"),
+                          torch.tensor([lk], dtype=torch.int32, device="cuda"),
+                          full.block_table, full.slot_mapping[h0:lk].contiguous())
+        ds.meta = W.StepMeta(np.array([0, lq], np.int32), np.array([lk], np.int32),
+                             meta.block_table, meta.slot_mapping[h0:lk], meta.num_blocks,
+                             meta.page_size, lq, lk)
+        G.note(f"chunk invariance: step Lq={lq} Lk={lk}")
+        outs.append(G.gpu_step(ds))
+    out_chunked = torch.cat(outs)
+    assert torch.equal(k0.view(torch.int16), full.k_cache.view(torch.int16))
+    assert torch.equal(v0.view(torch.int16), full.v_cache.view(torch.int16))
+    a, b = G.to_f64(out_chunked), G.to_f64(out_full)
+    G.compare(a, b, W.BF16, "chunked vs full")
+    rng = np.random.default_rng(5)
+    rows = sorted({0, 2047, 2048, 8191, 8192, 9999} | set(rng.choice(10000, 26, replace=False).tolist()))
+    sel = np.zeros(10000, np.uint8)
+    sel[rows] = 1
+    ref, _, _ = G.oracle_full(full, kc_host, vc_host, row_select=sel)
+    G.compare(a[rows], ref[rows], W.BF16, "chunked vs oracle")
+    G.compare(b[rows], ref[rows], W.BF16, "full vs oracle")
+    G.note(f"chunk invariance: chunked == full bitwise: {bool(np.array_equal(a, b))}")
+
+
+# ---------------------------------------------------------------- properties
+def test_repeat_is_deterministic():
+    spec, meta = W.make_step(2)
+    ds = W.device_values(spec, meta, seed=0)
+    G.note("determinism: config 2 twice")
+    a = G.gpu_step(ds)
+    b = G.gpu_step(ds)
+    import torch
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_segment_order_does_not_matter():
+    """Each segment sees only its own pages: packing the same segments in
+    another order gives bitwise the same rows."""
+    import torch
+    segs = [(1, 700), (90, 400), (1, 40), (1, 2500), (33, 33)]
+    spec, meta = W.custom_step(segs, 4, 4, 128, W.BF16, seed=31)
+    hs = W.host_values(spec, meta, seed=31, poison=False)
+    ds = _dev(hs)
+    G.note("segment order: original")
+    out = W.to_host_array(G.gpu_step(ds, append=False))
+    order = [3, 0, 4, 2, 1]
+    lq = np.diff(meta.cu_seqlens_q)
+    rows = np.concatenate([np.arange(meta.cu_seqlens_q[b], meta.cu_seqlens_q[b + 1]) for b in order])
+    cu = np.concatenate([[0], np.cumsum(lq[order])]).astype(np.int32)
+    ds2 = W.DeviceStep(spec, meta, ds.q[torch.from_numpy(rows).cuda()].contiguous(), None, None,
+                       ds.k_cache, ds.v_cache, torch.from_numpy(cu).cuda(),
+                       ds.seqlens_k[order].contiguous(), ds.block_table[order].contiguous(), None)
+    ds2.meta = W.StepMeta(cu, meta.seqlens_k[order], meta.block_table[order], None,
+                          meta.num_blocks, meta.page_size, meta.max_seqlen_q, meta.max_seqlen_k)
+    G.note("segment order: permuted")
+    out2 = W.to_host_array(G.gpu_step(ds2, append=False))
+    assert np.array_equal(out2, out[rows])
+
+
+def test_workspace_too_small_is_reported():
+    import torch
+    spec, meta = W.custom_step([(1, 100)], 2, 2, 64, W.F32, seed=1)
+    ds = _dev(W.host_values(spec, meta))
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(B.HybridAttnError) as e:
+        B.hybrid_attn_fwd(ds.q, ds.k_cache, ds.v_cache, ds.cu_seqlens_q, ds.seqlens_k,
+                          ds.block_table, 1, 100, workspace=ws)
+    assert e.value.status == B.HA_ERR_WORKSPACE_TOO_SMALL
