@@ -173,6 +173,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     a.hdr->split = split;
     a.hdr->bad_segments = s_bad;
     a.hdr->counter = 0;
+    a.hdr->dec_counter = 0;
   }
 }
 
@@ -245,7 +246,7 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int j, unsigned char
   unsigned char* Ks = smem;
   unsigned char* Vt = smem + BN * KROW;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int qc = lane & 31, g = lane >> 5;
   const int q0 = a.cu[seg], Lq = a.cu[seg + 1] - q0, Lk = a.sk[seg], H0 = Lk - Lq;
   const int ntiles = (Lq + kChunkRows - 1) / kChunkRows;
@@ -257,10 +258,6 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int j, unsigned char
   const int wrow0 = row0 + w * 32;
   const int my_row = wrow0 + qc;
   const bool wave_active = wrow0 < rows_end;
-  const int32_t* btrow = a.bt + static_cast<size_t>(seg) * a.max_blocks;
-  const bf16_t* kc = static_cast<const bf16_t*>(a.kc);
-  const bf16_t* vc = static_cast<const bf16_t*>(a.vc);
-  const size_t slot_elems = static_cast<size_t>(a.num_kv_heads) * D;
   const int pi = key_perm(qc);
 
   // Q^T operand: lane supplies Q[my_row][s*16 + g*8 .. +8]
@@ -278,55 +275,80 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int j, unsigned char
   for (int m = 0; m < NM; ++m) acc[m] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
 
+  // Tile loads.  Every 16-byte load of a tile reads from one page that is the
+  // same for the whole wave (K: load `it` covers page it (D=128) or
+  // 2*it + w/2 (D=64); V: wave w covers page w), so the pages are scalar
+  // loads from the block table and the gathers are buffer loads with a
+  // 32-bit lane offset.  Keys at or past kend read as zero (offset out of
+  // range, or an empty descriptor for whole pages).
+  const_i32_t* btrow = (const_i32_t*)(a.bt) + static_cast<size_t>(seg) * a.max_blocks;
+  const int last_page = (kend - 1) >> 4;
+  const uint32_t slot_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 2;
+  const uint32_t page_bytes = slot_bytes * kPage;
+  const uint32_t head_off = static_cast<uint32_t>(kvh) * D * 2;
+  unsigned char* kpool = const_cast<unsigned char*>(static_cast<const unsigned char*>(a.kc));
+  unsigned char* vpool = const_cast<unsigned char*>(static_cast<const unsigned char*>(a.vc));
+  const int vc_ = tid % CPR, vkg = tid / CPR;  // V transpose: chunk and key group of this thread
+  u32x4_t kreg[KLOADS], vreg[VKG];
+  auto issue_tile = [&](int k0) {
+    __amdgpu_buffer_rsrc_t kr[BN / 16], vr[BN / 16];
+#pragma unroll
+    for (int pp = 0; pp < BN / 16; ++pp) {
+      const int idx = (k0 >> 4) + pp;
+      const int id = btrow[min(idx, last_page)];
+      const bool ok = idx <= last_page && static_cast<unsigned>(id) < static_cast<unsigned>(a.num_blocks);
+      const size_t base = static_cast<size_t>(ok ? id : 0) * page_bytes;
+      const int n = ok ? static_cast<int>(page_bytes) : 0;
+      kr[pp] = __builtin_amdgcn_make_buffer_rsrc(kpool + base, 0, n, kRawBufferWord3);
+      vr[pp] = __builtin_amdgcn_make_buffer_rsrc(vpool + base, 0, n, kRawBufferWord3);
+    }
+#pragma unroll
+    for (int it = 0; it < KLOADS; ++it) {
+      const int key = (it * kThreads + tid) / CPR;
+      const int pidx = (it * kThreads + w * kWave) / (16 * CPR);  // uniform per wave
+      const uint32_t off = (k0 + key < kend)
+                               ? (key & 15) * slot_bytes + head_off + (tid % CPR) * 16
+                               : kOffsetOutOfRange;
+      kreg[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(kr[pidx], off, 0, 0));
+    }
+#pragma unroll
+    for (int t = 0; t < VKG; ++t) {
+      const int key = vkg * VKG + t;  // in page w of the tile
+      const uint32_t off = (k0 + key < kend)
+                               ? (key & 15) * slot_bytes + head_off + vc_ * 16
+                               : kOffsetOutOfRange;
+      vreg[t] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vr[w], off, 0, 0));
+    }
+  };
+
+  issue_tile(0);
   for (int k0 = 0; k0 < kend; k0 += BN) {
     __syncthreads();  // previous tile fully consumed
     // K tile, natural layout Ks[key][d]
 #pragma unroll
     for (int it = 0; it < KLOADS; ++it) {
       const int idx = it * kThreads + tid;
-      const int key = idx / CPR, c = idx % CPR, kp = k0 + key;
-      u32x4_t v = {0, 0, 0, 0};
-      if (kp < Lk) {
-        const int page = btrow[kp >> 4];
-        if (static_cast<unsigned>(page) < static_cast<unsigned>(a.num_blocks))
-          v = ld16(kc + (static_cast<size_t>(page) * kPage + (kp & 15)) * slot_elems +
-                   static_cast<size_t>(kvh) * D + c * 8);
-      }
-      st16(Ks + key * KROW + c * 16, v);
+      st16(Ks + (idx / CPR) * KROW + (idx % CPR) * 16, kreg[it]);
     }
-    // V tile, transposed: Vt[d][key]; thread owns chunk c (8 channels) of VKG keys
-    {
-      const int c = tid % CPR, kg = tid / CPR;
-      u32x4_t v[VKG];
+    // V tile, transposed: Vt[d][key]; thread owns chunk vc_ (8 channels) of VKG keys
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t hv[VKG];
 #pragma unroll
       for (int t = 0; t < VKG; ++t) {
-        const int kp = k0 + kg * VKG + t;
-        v[t] = u32x4_t{0, 0, 0, 0};
-        if (kp < Lk) {
-          const int page = btrow[kp >> 4];
-          if (static_cast<unsigned>(page) < static_cast<unsigned>(a.num_blocks))
-            v[t] = ld16(vc + (static_cast<size_t>(page) * kPage + (kp & 15)) * slot_elems +
-                        static_cast<size_t>(kvh) * D + c * 8);
-        }
+        const uint32_t word = vreg[t][e >> 1];
+        hv[t] = (e & 1) ? (word >> 16) : (word & 0xffffu);
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t hv[VKG];
-#pragma unroll
-        for (int t = 0; t < VKG; ++t) {
-          const uint32_t word = v[t][e >> 1];
-          hv[t] = (e & 1) ? (word >> 16) : (word & 0xffffu);
-        }
-        unsigned char* dst = Vt + (c * 8 + e) * VROW + kg * VKG * 2;
-        if constexpr (VKG == 4) {
-          st8(dst, u32x2_t{hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)});
-        } else {
-          static_assert(VKG == 2, "V transpose handles 2 or 4 keys per thread");
-          *reinterpret_cast<uint32_t*>(dst) = hv[0] | (hv[1] << 16);
-        }
+      unsigned char* dst = Vt + (vc_ * 8 + e) * VROW + vkg * VKG * 2;
+      if constexpr (VKG == 4) {
+        st8(dst, u32x2_t{hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)});
+      } else {
+        static_assert(VKG == 2, "V transpose handles 2 or 4 keys per thread");
+        *reinterpret_cast<uint32_t*>(dst) = hv[0] | (hv[1] << 16);
       }
     }
     __syncthreads();
+    issue_tile(k0 + BN);  // next tile streams in while this one is computed
     if (!wave_active || k0 > H0 + wrow0 + 31) continue;  // tile invisible to this wave
     const bool need_mask = (k0 + BN - 1) > (H0 + wrow0);
 
@@ -415,7 +437,7 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int j, unsigned char*
   float* Ks = reinterpret_cast<float*>(smem);
   float* Vs = Ks + BN * ROWF;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int qc = lane & 31, g = lane >> 5;
   const int q0 = a.cu[seg], Lq = a.cu[seg + 1] - q0, Lk = a.sk[seg], H0 = Lk - Lq;
   const int ntiles = (Lq + kChunkRows - 1) / kChunkRows;
@@ -427,10 +449,6 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int j, unsigned char*
   const int wrow0 = row0 + w * 32;
   const int my_row = wrow0 + qc;
   const bool wave_active = wrow0 < rows_end;
-  const int32_t* btrow = a.bt + static_cast<size_t>(seg) * a.max_blocks;
-  const float* kc = static_cast<const float*>(a.kc);
-  const float* vc = static_cast<const float*>(a.vc);
-  const size_t slot_elems = static_cast<size_t>(a.num_kv_heads) * D;
   const int pi = key_perm(qc);
 
   float qf[KS];  // lane supplies Q[my_row][2s + g]
@@ -446,26 +464,51 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int j, unsigned char*
   for (int m = 0; m < NM; ++m) acc[m] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
 
+  // Tile loads as in the bf16 role: load `it` of every thread reads one page,
+  // uniform per wave, through a buffer descriptor; keys at or past kend read 0.
+  const_i32_t* btrow = (const_i32_t*)(a.bt) + static_cast<size_t>(seg) * a.max_blocks;
+  const int last_page = (kend - 1) >> 4;
+  const uint32_t slot_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 4;
+  const uint32_t page_bytes = slot_bytes * kPage;
+  const uint32_t head_off = static_cast<uint32_t>(kvh) * D * 4;
+  unsigned char* kpool = const_cast<unsigned char*>(static_cast<const unsigned char*>(a.kc));
+  unsigned char* vpool = const_cast<unsigned char*>(static_cast<const unsigned char*>(a.vc));
+  u32x4_t kreg[LOADS], vreg[LOADS];
+  auto issue_tile = [&](int k0) {
+    __amdgpu_buffer_rsrc_t kr[BN / 16], vr[BN / 16];
+#pragma unroll
+    for (int pp = 0; pp < BN / 16; ++pp) {
+      const int idx = (k0 >> 4) + pp;
+      const int id = btrow[min(idx, last_page)];
+      const bool ok = idx <= last_page && static_cast<unsigned>(id) < static_cast<unsigned>(a.num_blocks);
+      const size_t base = static_cast<size_t>(ok ? id : 0) * page_bytes;
+      const int n = ok ? static_cast<int>(page_bytes) : 0;
+      kr[pp] = __builtin_amdgcn_make_buffer_rsrc(kpool + base, 0, n, kRawBufferWord3);
+      vr[pp] = __builtin_amdgcn_make_buffer_rsrc(vpool + base, 0, n, kRawBufferWord3);
+    }
+#pragma unroll
+    for (int it = 0; it < LOADS; ++it) {
+      const int key = (it * kThreads + tid) / CPR;
+      const int pidx = (it * kThreads + w * kWave) / (16 * CPR);  // uniform per wave
+      const uint32_t off = (k0 + key < kend)
+                               ? (key & 15) * slot_bytes + head_off + (tid % CPR) * 16
+                               : kOffsetOutOfRange;
+      kreg[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(kr[pidx], off, 0, 0));
+      vreg[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vr[pidx], off, 0, 0));
+    }
+  };
+
+  issue_tile(0);
   for (int k0 = 0; k0 < kend; k0 += BN) {
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
       const int idx = it * kThreads + tid;
-      const int key = idx / CPR, c = idx % CPR, kp = k0 + key;
-      u32x4_t kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-      if (kp < Lk) {
-        const int page = btrow[kp >> 4];
-        if (static_cast<unsigned>(page) < static_cast<unsigned>(a.num_blocks)) {
-          const size_t off = (static_cast<size_t>(page) * kPage + (kp & 15)) * slot_elems +
-                             static_cast<size_t>(kvh) * D + c * 4;
-          kv = ld16(kc + off);
-          vv = ld16(vc + off);
-        }
-      }
-      st16(Ks + key * ROWF + c * 4, kv);
-      st16(Vs + key * ROWF + c * 4, vv);
+      st16(Ks + (idx / CPR) * ROWF + (idx % CPR) * 4, kreg[it]);
+      st16(Vs + (idx / CPR) * ROWF + (idx % CPR) * 4, vreg[it]);
     }
     __syncthreads();
+    issue_tile(k0 + BN);
     if (!wave_active || k0 > H0 + wrow0 + 31) continue;
     const bool need_mask = (k0 + BN - 1) > (H0 + wrow0);
 
@@ -592,7 +635,7 @@ __device__ void decode_item(const MainArgs& a, int seg, int j, int split_keys) {
   constexpr int EPL = D / 16;  // channels per lane
   using Frag = RowFrag<T, EPL>;
   constexpr bool kLateV = Frag::kWords > 4;  // fp32 D=128: load V after the scores
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
   const int head_groups = (a.num_heads + kHeadsPerDecodeItem - 1) / kHeadsPerDecodeItem;
   const int split = j / head_groups, hg = j - split * head_groups;
   const int h = hg * kHeadsPerDecodeItem + w;
@@ -707,18 +750,244 @@ __device__ void decode_item(const MainArgs& a, int seg, int j, int split_keys) {
   }
 }
 
+// ---------------------------------------------------------------- decode role, bf16
+// Same lane layout as decode_item, tuned for bf16: scores with v_dot2_f32_bf16
+// on the raw bf16 pairs, the 16-lane reduce-scatter and the weight broadcast
+// on DPP row operations, P.V on bf16 pairs (weights rounded to bf16, the sum of
+// weights taken from the same rounded values), and the K / V loads of the next
+// 64-key step issued while the current one is being reduced, so every wave
+// keeps up to 32 16-byte loads in flight.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppQuadReverse>(v));
+  v = fmaxf(v, dpp_f32<kDppQuadSwap>(v));
+  return v;
+}
+
+template <int WPL>
+struct KvStep {  // one 64-key step of one pool: 16 key rows x WPL words per lane
+  uint32_t w[16][WPL];
+};
+
+// Loads one 64-key step of one pool for this lane: key rows kb + 4u + r,
+// u = 0..15, channels of lane column c.  The four pages of the step are
+// addressed through buffer descriptors (base in SGPRs, 32-bit lane offset):
+// the hardware range check returns zeros for pages past the split, for block
+// ids outside the pool (descriptor of size 0) and for the lanes whose key is
+// past the end of the split (offset moved out of range), without branches.
+template <int WPL>
+__device__ __forceinline__ void load_step(KvStep<WPL>& dst, const unsigned char* pool,
+                                          const_i32_t* btrow, int kb, int kfin, int num_blocks,
+                                          uint32_t page_bytes, uint32_t lane_off,
+                                          uint32_t row4_bytes, int r) {
+  __amdgpu_buffer_rsrc_t rs[4];
+  const int last_page = (kfin - 1) >> 4;  // block-table index of the split's last key
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    const int idx = (kb >> 4) + pp;
+    const int id = btrow[min(idx, last_page)];  // scalar load, always inside the row
+    const int pg = idx <= last_page ? id : -1;
+    const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(num_blocks);
+    rs[pp] = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(pool) + static_cast<size_t>(ok ? pg : 0) * page_bytes, 0,
+        ok ? static_cast<int>(page_bytes) : 0, kRawBufferWord3);
+  }
+  const bool full = kb + 64 <= kfin;
+  const int lim = kfin - kb - r;  // rows 4u + r of this lane are in the split while 4u < lim
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const uint32_t vo = (full || 4 * u < lim) ? lane_off : kOffsetOutOfRange;
+    const uint32_t so = (u & 3) * row4_bytes;
+    if constexpr (WPL == 4) {
+      const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs[u >> 2], vo, so, 0));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst.w[u][i] = v[i];
+    } else {
+      const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs[u >> 2], vo, so, 0));
+      dst.w[u][0] = v[0];
+      dst.w[u][1] = v[1];
+    }
+  }
+}
+
+template <int D>
+__device__ void decode_item_bf16(const MainArgs& a, int seg, int j, int split_keys) {
+  constexpr int WPL = D / 32;  // bf16 pairs per lane per key row (8 or 4 channels)
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int head_groups = (a.num_heads + kHeadsPerDecodeItem - 1) / kHeadsPerDecodeItem;
+  const int split = j / head_groups, hg = j - split * head_groups;
+  const int h = hg * kHeadsPerDecodeItem + w;
+  if (h >= a.num_heads) return;
+  const int row = a.cu[seg], Lk = a.sk[seg];
+  const int nsplit = (Lk + split_keys - 1) / split_keys;
+  const int kbeg = split * split_keys, kfin = min(Lk, kbeg + split_keys);
+  const int r = lane >> 4, c = lane & 15;
+  const int kvh = h / a.group;
+  const_i32_t* btrow = (const_i32_t*)(a.bt) + static_cast<size_t>(seg) * a.max_blocks;
+  const uint32_t slot_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 2;
+  const uint32_t page_bytes = slot_bytes * kPage;
+  const uint32_t lane_off = r * slot_bytes + static_cast<uint32_t>(kvh) * D * 2 + c * WPL * 4;
+  const uint32_t row4_bytes = 4 * slot_bytes;
+  const unsigned char* kpool = static_cast<const unsigned char*>(a.kc);
+  const unsigned char* vpool = static_cast<const unsigned char*>(a.vc);
+
+  uint32_t qw[WPL];
+  {
+    const unsigned char* qp = static_cast<const unsigned char*>(a.q) +
+                              (static_cast<size_t>(row) * a.num_heads + h) * D * 2 + c * WPL * 4;
+    if constexpr (WPL == 4) {
+      const u32x4_t v = ld16(qp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qw[i] = v[i];
+    } else {
+      const u32x2_t v = ld8(qp);
+      qw[0] = v[0];
+      qw[1] = v[1];
+    }
+  }
+  float m_run = -INFINITY, l_lane = 0.f, acc[2 * WPL];
+#pragma unroll
+  for (int e = 0; e < 2 * WPL; ++e) acc[e] = 0.f;
+
+  KvStep<WPL> kst, vst;
+  load_step<WPL>(kst, kpool, btrow, kbeg, kfin, a.num_blocks, page_bytes, lane_off, row4_bytes, r);
+  load_step<WPL>(vst, vpool, btrow, kbeg, kfin, a.num_blocks, page_bytes, lane_off, row4_bytes, r);
+  for (int kb = kbeg; kb < kfin; kb += 64) {
+    // partial dot products: this lane's channels of key rows 4u + r
+    float pu[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      float sdot = 0.f;
+#pragma unroll
+      for (int i = 0; i < WPL; ++i) sdot = dot2_bf16(kst.w[u][i], qw[i], sdot);
+      pu[u] = sdot;
+    }
+    // K registers are free: start the next step's K (past the split every
+    // descriptor is empty and the loads return zeros without touching memory)
+    load_step<WPL>(kst, kpool, btrow, kb + 64, kfin, a.num_blocks, page_bytes, lane_off,
+                   row4_bytes, r);
+    // reduce-scatter over the 16 lanes of the row: lane c ends with key row u = c
+    {
+      const bool up8 = (c & 8) != 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float send = up8 ? pu[i] : pu[i + 8];
+        const float keep = up8 ? pu[i + 8] : pu[i];
+        pu[i] = keep + dpp_f32<kDppRowMirror>(send);
+      }
+      const bool up4 = (c & 4) != 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float send = up4 ? pu[i] : pu[i + 4];
+        const float keep = up4 ? pu[i + 4] : pu[i];
+        pu[i] = keep + dpp_f32<kDppRowHalfMirror>(send);
+      }
+      const bool up2 = (c & 2) != 0;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float send = up2 ? pu[i] : pu[i + 2];
+        const float keep = up2 ? pu[i + 2] : pu[i];
+        pu[i] = keep + dpp_f32<kDppQuadReverse>(send);
+      }
+      const bool up1 = (c & 1) != 0;
+      const float send = up1 ? pu[0] : pu[1];
+      const float keep = up1 ? pu[1] : pu[0];
+      pu[0] = keep + dpp_f32<kDppQuadSwap>(send);
+    }
+    const int my_key = kb + 4 * c + r;
+    const float s = my_key < kfin ? pu[0] * a.scale_log2 : -INFINITY;
+    float mx = row16_max(s);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);  // finite: key kb is in range
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    // this lane's weight rounded to bf16; pairs (key rows 2t, 2t+1) formed on even lanes
+    const uint32_t pbits = pack_bf16x2(fast_exp2(s - m_new), 0.f) & 0xffffu;
+    l_lane = l_lane * alpha + __uint_as_float(pbits << 16);
+    const uint32_t pair = pbits | (dpp_u32<kDppQuadSwap>(pbits) << 16);
+#pragma unroll
+    for (int e = 0; e < 2 * WPL; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      uint32_t pw;
+      switch (t) {  // row_newbcast needs a compile-time lane
+        case 0: pw = dpp_u32<kDppRowBcast0 + 0>(pair); break;
+        case 1: pw = dpp_u32<kDppRowBcast0 + 2>(pair); break;
+        case 2: pw = dpp_u32<kDppRowBcast0 + 4>(pair); break;
+        case 3: pw = dpp_u32<kDppRowBcast0 + 6>(pair); break;
+        case 4: pw = dpp_u32<kDppRowBcast0 + 8>(pair); break;
+        case 5: pw = dpp_u32<kDppRowBcast0 + 10>(pair); break;
+        case 6: pw = dpp_u32<kDppRowBcast0 + 12>(pair); break;
+        default: pw = dpp_u32<kDppRowBcast0 + 14>(pair); break;
+      }
+#pragma unroll
+      for (int i = 0; i < WPL; ++i) {
+        const uint32_t v0 = vst.w[2 * t][i], v1 = vst.w[2 * t + 1][i];
+        acc[2 * i] = dot2_bf16(pw, pair_lo(v0, v1), acc[2 * i]);
+        acc[2 * i + 1] = dot2_bf16(pw, pair_hi(v0, v1), acc[2 * i + 1]);
+      }
+    }
+    load_step<WPL>(vst, vpool, btrow, kb + 64, kfin, a.num_blocks, page_bytes, lane_off,
+                   row4_bytes, r);
+  }
+
+  const float l_tot = wave_sum(l_lane);
+#pragma unroll
+  for (int e = 0; e < 2 * WPL; ++e) {
+    acc[e] += __shfl_xor(acc[e], 16);
+    acc[e] += __shfl_xor(acc[e], 32);
+  }
+  if (nsplit == 1) {
+    if (r == 0) {
+      const float inv = 1.f / l_tot;
+      float o[2 * WPL];
+#pragma unroll
+      for (int e = 0; e < 2 * WPL; ++e) o[e] = acc[e] * inv;
+      store_row<bf16_t, 2 * WPL>(static_cast<bf16_t*>(a.out) +
+                                     (static_cast<size_t>(row) * a.num_heads + h) * D + c * 2 * WPL, o);
+    }
+  } else {
+    float* pp = a.partials +
+                (static_cast<size_t>(a.part_prefix[seg] + split) * a.num_heads + h) * a.part_stride;
+    if (r == 0) store_row<float, 2 * WPL>(pp + 4 + c * 2 * WPL, acc);
+    if (lane == 0) {
+      pp[0] = m_run;
+      pp[1] = l_tot;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- persistent kernel
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void attn_kernel(MainArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
   constexpr int kSmem = ChunkCfg<T>::template Sizes<D>::BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kSmem];
   __shared__ int s_work[3];
   const int n_chunk = a.hdr->n_chunk_items;
-  const int n_total = n_chunk + a.hdr->n_dec_items;
+  const int n_dec = a.hdr->n_dec_items;
+  const int n_total = n_chunk + n_dec;
   const int split_keys = a.hdr->split;
+  // Two queues: the first half of the workgroups takes chunk tiles while any
+  // are left, the second half decode splits; each falls back to the other
+  // queue when its own is empty.  Both roles therefore run side by side on
+  // every CU from the start of the launch.
+  const bool chunk_first = blockIdx.x < (gridDim.x + 1) / 2;
+  bool chunk_open = true, dec_open = true;  // meaningful in thread 0 only
   for (;;) {
     if (threadIdx.x == 0) {
-      const int it = static_cast<int>(atomicAdd(&a.hdr->counter, 1u));
+      int it = n_total;
+      for (int attempt = 0; attempt < 2 && it == n_total; ++attempt) {
+        const bool want_chunk = (attempt == 0) == chunk_first;
+        if (want_chunk && chunk_open) {
+          const int c = static_cast<int>(atomicAdd(&a.hdr->counter, 1u));
+          if (c < n_chunk) it = c; else chunk_open = false;
+        } else if (!want_chunk && dec_open) {
+          const int d = static_cast<int>(atomicAdd(&a.hdr->dec_counter, 1u));
+          if (d < n_dec) it = n_chunk + d; else dec_open = false;
+        }
+      }
       int seg = 0, local = 0;
       if (it < n_chunk) {
         seg = find_segment(a.chunk_prefix, a.num_seqs, it);
@@ -732,49 +1001,72 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(MainArgs a) {
       s_work[2] = local;
     }
     __syncthreads();
-    const int it = s_work[0], seg = s_work[1], local = s_work[2];
+    // the work item is uniform across the workgroup: keep it in scalar registers so
+    // every address derived from it (segment row, block-table row, pages) is scalar
+    const int it = __builtin_amdgcn_readfirstlane(s_work[0]);
+    const int seg = __builtin_amdgcn_readfirstlane(s_work[1]);
+    const int local = __builtin_amdgcn_readfirstlane(s_work[2]);
     __syncthreads();
     if (it >= n_total) break;
     if (it < n_chunk) {
       if constexpr (sizeof(T) == 2) chunk_tile_bf16<D>(a, seg, local, smem);
       else chunk_tile_f32<D>(a, seg, local, smem);
     } else {
-      decode_item<T, D>(a, seg, local, split_keys);
+      if constexpr (sizeof(T) == 2) decode_item_bf16<D>(a, seg, local, split_keys);
+      else decode_item<T, D>(a, seg, local, split_keys);
     }
   }
 }
 
 // ---------------------------------------------------------------- combine
+// One wave per (decode segment, head) that was split: lanes first reduce the
+// split maxima, then every lane owns D / 64 channels and sums the rescaled
+// partial accumulators of all splits.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void combine_kernel(MainArgs a) {
-  const int seg = blockIdx.x;
+  const int head_groups = (a.num_heads + kHeadsPerDecodeItem - 1) / kHeadsPerDecodeItem;
+  const int seg = blockIdx.x / head_groups, hg = blockIdx.x - seg * head_groups;
   const int p0 = a.part_prefix[seg], np = a.part_prefix[seg + 1] - p0;
   if (np <= 0) return;
   constexpr int EPL = D / kWave;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int h = hg * kHeadsPerDecodeItem + w;
+  if (h >= a.num_heads) return;
   const int row = a.cu[seg];
-  for (int h = w; h < a.num_heads; h += kThreads / kWave) {
-    const float* base = a.partials + (static_cast<size_t>(p0) * a.num_heads + h) * a.part_stride;
-    const size_t step = static_cast<size_t>(a.num_heads) * a.part_stride;
-    float mx = -INFINITY;
-    for (int s = 0; s < np; ++s) mx = fmaxf(mx, base[s * step]);
-    float l = 0.f, o[EPL];
+  const size_t step = static_cast<size_t>(a.num_heads) * a.part_stride;
+  const float* base = a.partials + (static_cast<size_t>(p0) * a.num_heads + h) * a.part_stride;
+  float mx = -INFINITY;
+  for (int sp = lane; sp < np; sp += kWave) mx = fmaxf(mx, base[sp * step]);
+  mx = wave_max(mx);
+  float l = 0.f, o[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-    for (int s = 0; s < np; ++s) {
-      const float* pp = base + s * step;
-      const float wgt = fast_exp2(pp[0] - mx);
-      l = fmaf(pp[1], wgt, l);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) o[e] = fmaf(pp[4 + lane * EPL + e], wgt, o[e]);
+  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+  for (int s0 = 0; s0 < np; s0 += kWave) {
+    const int sp = s0 + lane;
+    float wgt = 0.f;
+    if (sp < np) {
+      wgt = fast_exp2(base[sp * step] - mx);
+      l = fmaf(base[sp * step + 1], wgt, l);
     }
-    const float inv = 1.f / l;
-    T* op = static_cast<T*>(a.out) + (static_cast<size_t>(row) * a.num_heads + h) * D + lane * EPL;
+    const int n = min(kWave, np - s0);
+    for (int t = 0; t < n; ++t) {
+      const float wt = __shfl(wgt, t);
+      const float* pp = base + (s0 + t) * step + 4 + lane * EPL;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      if constexpr (sizeof(T) == 2) op[e] = static_cast<bf16_t>(f32_to_bf16_rne(o[e] * inv));
-      else op[e] = o[e] * inv;
+      for (int e = 0; e < EPL; ++e) o[e] = fmaf(pp[e], wt, o[e]);
     }
+  }
+  const float inv = 1.f / wave_sum(l);
+  T* op = static_cast<T*>(a.out) + (static_cast<size_t>(row) * a.num_heads + h) * D + lane * EPL;
+  if constexpr (sizeof(T) == 2) {
+    if constexpr (EPL == 2) {
+      *reinterpret_cast<uint32_t*>(op) = pack_bf16x2(o[0] * inv, o[1] * inv);
+    } else {
+      *op = static_cast<bf16_t>(pack_bf16x2(o[0] * inv, 0.f) & 0xffffu);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) op[e] = o[e] * inv;
   }
 }
 
@@ -815,7 +1107,8 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dt, int di) {
               chunk_prefix, dec_prefix, part_prefix,
               reinterpret_cast<float*>(ws + L.ws.partials)};
   hipLaunchKernelGGL((attn_kernel<T, D>), dim3(grid), dim3(kThreads), 0, L.stream, ma);
-  hipLaunchKernelGGL((combine_kernel<T, D>), dim3(L.num_seqs), dim3(kThreads), 0, L.stream, ma);
+  hipLaunchKernelGGL((combine_kernel<T, D>), dim3(L.num_seqs * head_groups), dim3(kThreads), 0,
+                     L.stream, ma);
   return hipGetLastError();
 }
 

@@ -12,6 +12,9 @@ constexpr int kPage = 16;         // tokens per KV page (the only page size supp
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef uint16_t bf16_t;  // storage type of bfloat16 (upper half of an fp32)
+// int32 data the kernels only read (block tables): viewed through the constant
+// address space so uniform reads become scalar loads.
+typedef const __attribute__((address_space(4))) int32_t const_i32_t;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -32,8 +35,38 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
 }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// Two fp32 -> packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// a.lo * b.lo + a.hi * b.hi + c on bf16 pairs, fp32 accumulate (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+// Bytes [a.lo16, b.lo16] and [a.hi16, b.hi16] of two bf16 pairs.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// ---- DPP lane exchanges inside rows of 16 lanes ---------------------------------------
+constexpr int kDppRowMirror = 0x140;      // lane c <- lane 15 - c
+constexpr int kDppRowHalfMirror = 0x141;  // lane c <- lane (c & 8) | (7 - (c & 7))
+constexpr int kDppQuadReverse = 0x1B;     // quad_perm [3,2,1,0]
+constexpr int kDppQuadSwap = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppRowBcast0 = 0x150;      // row_newbcast:n -> every lane gets lane n of its row
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kCtrl, 0xf, 0xf, false));
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<kCtrl>(__float_as_uint(v)));
 }
 
 // Element traits: T is float (fp32 storage) or bf16_t.
@@ -47,11 +80,22 @@ template <> struct Elem<bf16_t> {
   __device__ static float to_f32(bf16_t x) { return bf16_to_f32(x); }
 };
 
+// ---- buffer descriptors ---------------------------------------------------------------
+// Word 3 of a raw (untyped, stride 0) buffer descriptor on the gfx9 family.
+constexpr int kRawBufferWord3 = 0x00020000;
+// A buffer offset past every descriptor's range: loads return 0.
+constexpr uint32_t kOffsetOutOfRange = 0x80000000u;
+
 // ---- 16-byte global / LDS accesses ------------------------------------------------
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
 __device__ __forceinline__ u32x2_t ld8(const void* p) { return *reinterpret_cast<const u32x2_t*>(p); }
 __device__ __forceinline__ void st8(void* p, u32x2_t v) { *reinterpret_cast<u32x2_t*>(p) = v; }
+
+// Index of this wave in its workgroup, as a scalar (uniform) value.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+}
 
 // ---- wave reductions (64 lanes) --------------------------------------------------
 __device__ __forceinline__ float wave_max(float v) {

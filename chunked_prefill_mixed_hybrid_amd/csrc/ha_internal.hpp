@@ -23,13 +23,14 @@ constexpr int kMaxSeqlenK = 1 << 30;
 // [header 256 B][chunk_prefix (B+1)][dec_prefix (B+1)][part_prefix (B+1)]
 // [partials parts_cap x H x (D + 4) fp32]; every array starts on a 256-byte boundary.
 struct PlanHeader {
-  uint32_t counter;       // next work item (reset to 0 by the planner each call)
+  uint32_t counter;       // next chunk-tile item (reset to 0 by the planner each call)
+  uint32_t dec_counter;   // next decode item (reset to 0 by the planner each call)
   int32_t n_chunk_items;  // items [0, n_chunk_items) are chunk tiles
   int32_t n_dec_items;    // items [n_chunk_items, +n_dec_items) are decode splits
   int32_t split;          // decode split size in keys (multiple of 64)
   int32_t n_parts;        // partial slots in use
   int32_t bad_segments;   // segments skipped because they broke a precondition
-  int32_t pad[58];
+  int32_t pad[57];
 };
 static_assert(sizeof(PlanHeader) == 256, "header is 256 bytes");
 
