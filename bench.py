@@ -49,6 +49,26 @@ def algorithmic_work(meta, spec):
             "step_bytes": kv_bytes + qo_bytes + append_bytes + meta_bytes}
 
 
+def profiled_traffic(workload_name):
+    """HBM bytes per attn_kernel launch from the committed rocprofv3 counter
+    summary of this workload, or None when there is none or the kernel sources
+    changed since the counters were taken."""
+    import hashlib
+    from pathlib import Path
+    root = Path(__file__).resolve().parent
+    prof = root / "profiles" / f"attn_kernel_{workload_name.replace('mixed_', 'mixed_')}.txt"
+    if not prof.exists():
+        return None
+    fields = dict(line.split(": ", 1) for line in prof.read_text().splitlines()
+                  if line.startswith(("source_sha256: ", "traffic_bytes: ")))
+    h = hashlib.sha256()
+    for src in ("attention.hip", "ha_common.hpp", "ha_internal.hpp"):
+        h.update((root / "chunked_prefill_mixed_hybrid_amd" / "csrc" / src).read_bytes())
+    if fields.get("source_sha256") != h.hexdigest():
+        return None
+    return float(fields["traffic_bytes"])
+
+
 def cpu_baseline(ds, spec, meta, budget_s=10.0):
     """The oracle (as it stands) on the host cores: the whole step (append +
     attention for every row), repeated until about budget_s of CPU time."""
@@ -80,6 +100,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra steps each preceded by a 1 GiB cache-flush write")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
@@ -111,11 +133,21 @@ def main():
             step()
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps back to back on one stream
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # timed region: exactly K steps back to back on one stream, nothing else enqueued
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = t_start.elapsed_time(t_end)
+
+    # per-call durations (HIP events on the stream the kernels run on), a second pass
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for e0, e1, e2 in ev:
         e0.record(stream)
         B.paged_kv_append(ds.key, ds.value, ds.slot_mapping, ds.k_cache, ds.v_cache, stream=stream)
@@ -125,7 +157,6 @@ def main():
                           workspace=ws, stream=stream)
         e2.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     attn_ms = np.array([e1.elapsed_time(e2) for _, e1, e2 in ev])
     append_ms = np.array([e0.elapsed_time(e1) for e0, e1, _ in ev])
 
@@ -140,6 +171,14 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1))
+
+    if args.calibrate_copy:  # a copy of known size: reads 1 GiB, writes 1 GiB
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     w = algorithmic_work(meta, spec)
     us_step = 1e6 * wall / args.steps
@@ -157,8 +196,9 @@ def main():
         achieved = w["flops"] / (attn_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_tf,
                 "unit": "TFLOP/s", "frac": round(achieved / peak_tf, 4), "traffic": None}
-    roof["kernel"] = "hybrid_attn_fwd (plan + attn + combine launches)"
+    roof["kernel"] = "hybrid_attn_fwd (plan_kernel + attn_kernel + combine_kernel, back to back)"
     roof["avg_us"] = round(attn_us, 2)
+    roof["traffic"] = profiled_traffic(spec.name)
 
     result = {
         "metric": METRIC, "value": round(us_step, 2), "unit": "us/step", "n_gpus": 1,
@@ -170,6 +210,7 @@ def main():
                    "head_dim": spec.head_dim, "page_size": meta.page_size,
                    "max_seqlen_q": meta.max_seqlen_q, "max_seqlen_k": meta.max_seqlen_k,
                    "seed": args.seed},
+        "gpu_us_per_step": round(1e3 * gpu_ms / args.steps, 2),
         "tflops": round(w["flops"] / (us_step * 1e-6) / 1e12, 2),
         "kv_gbps": round(w["kv_bytes"] / (us_step * 1e-6) / 1e9, 1),
         "step_gbps": round(w["step_bytes"] / (us_step * 1e-6) / 1e9, 1),
