@@ -40,7 +40,7 @@ struct PlanArgs {
   const int32_t* cu;
   const int32_t* sk;
   int num_seqs, total_q, max_q, max_k, max_blocks, num_heads, head_groups, parts_cap,
-      target_items;
+      target_items, grid;
   PlanHeader* hdr;
   int32_t* chunk_prefix;
   int32_t* dec_prefix;
@@ -172,8 +172,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     a.hdr->n_parts = s_carry[2];
     a.hdr->split = split;
     a.hdr->bad_segments = s_bad;
-    a.hdr->counter = 0;
-    a.hdr->dec_counter = 0;
+    // the attention kernel hands out the first item of every workgroup statically:
+    // chunk items [0, half) to the first half, decode items [0, grid - half) to the rest
+    const int half = (a.grid + 1) / 2;
+    a.hdr->counter = static_cast<uint32_t>(min(s_carry[0], half));
+    a.hdr->dec_counter = static_cast<uint32_t>(min(s_carry[1], a.grid - half));
   }
 }
 
@@ -290,34 +293,33 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int j, unsigned char
   unsigned char* vpool = const_cast<unsigned char*>(static_cast<const unsigned char*>(a.vc));
   const int vc_ = tid % CPR, vkg = tid / CPR;  // V transpose: chunk and key group of this thread
   u32x4_t kreg[KLOADS], vreg[VKG];
+  // Descriptor of page `pidx` of the tile starting at key k0 (uniform pidx);
+  // empty past kend or for a block id outside the pool.
+  auto page_rsrc = [&](unsigned char* pool, int k0, int pidx) {
+    const int idx = (k0 >> 4) + pidx;
+    const int id = btrow[min(idx, last_page)];
+    const bool ok = idx <= last_page && static_cast<unsigned>(id) < static_cast<unsigned>(a.num_blocks);
+    return __builtin_amdgcn_make_buffer_rsrc(pool + static_cast<size_t>(ok ? id : 0) * page_bytes, 0,
+                                             ok ? static_cast<int>(page_bytes) : 0, kRawBufferWord3);
+  };
   auto issue_tile = [&](int k0) {
-    __amdgpu_buffer_rsrc_t kr[BN / 16], vr[BN / 16];
-#pragma unroll
-    for (int pp = 0; pp < BN / 16; ++pp) {
-      const int idx = (k0 >> 4) + pp;
-      const int id = btrow[min(idx, last_page)];
-      const bool ok = idx <= last_page && static_cast<unsigned>(id) < static_cast<unsigned>(a.num_blocks);
-      const size_t base = static_cast<size_t>(ok ? id : 0) * page_bytes;
-      const int n = ok ? static_cast<int>(page_bytes) : 0;
-      kr[pp] = __builtin_amdgcn_make_buffer_rsrc(kpool + base, 0, n, kRawBufferWord3);
-      vr[pp] = __builtin_amdgcn_make_buffer_rsrc(vpool + base, 0, n, kRawBufferWord3);
-    }
 #pragma unroll
     for (int it = 0; it < KLOADS; ++it) {
       const int key = (it * kThreads + tid) / CPR;
-      const int pidx = (it * kThreads + w * kWave) / (16 * CPR);  // uniform per wave
       const uint32_t off = (k0 + key < kend)
                                ? (key & 15) * slot_bytes + head_off + (tid % CPR) * 16
                                : kOffsetOutOfRange;
-      kreg[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(kr[pidx], off, 0, 0));
+      const auto rs = page_rsrc(kpool, k0, (it * kThreads + w * kWave) / (16 * CPR));
+      kreg[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
     }
+    const auto rs = page_rsrc(vpool, k0, w);  // V keys of wave w all sit in page w of the tile
 #pragma unroll
     for (int t = 0; t < VKG; ++t) {
-      const int key = vkg * VKG + t;  // in page w of the tile
+      const int key = vkg * VKG + t;
       const uint32_t off = (k0 + key < kend)
                                ? (key & 15) * slot_bytes + head_off + vc_ * 16
                                : kOffsetOutOfRange;
-      vreg[t] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vr[w], off, 0, 0));
+      vreg[t] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
     }
   };
 
@@ -358,8 +360,11 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int j, unsigned char
     for (int kb = 0; kb < NKB; ++kb) {
       sacc[kb] = f32x16_t{};
       const unsigned char* kr = Ks + (kb * 32 + pi) * KROW + g * 16;
+      u32x4_t kf[KS];  // all K fragments of the block first, then the MFMA chain
 #pragma unroll
-      for (int s = 0; s < KS; ++s) sacc[kb] = mfma_bf16(ld16(kr + s * 32), qf[s], sacc[kb]);
+      for (int s = 0; s < KS; ++s) kf[s] = ld16(kr + s * 32);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) sacc[kb] = mfma_bf16(kf[s], qf[s], sacc[kb]);
     }
     // scale (base 2), causal mask on diagonal tiles, running max
     float tmax = -INFINITY;
@@ -403,11 +408,15 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int j, unsigned char
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const unsigned char* vr = Vt + (m * 32 + qc) * VROW + g * 16;
+      u32x4_t vf[NKB][2];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) acc[m] = mfma_bf16(ld16(vr + (kb * 32 + u * 16) * 2), pk[kb][u], acc[m]);
-      }
+        for (int u = 0; u < 2; ++u) vf[kb][u] = ld16(vr + (kb * 32 + u * 16) * 2);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) acc[m] = mfma_bf16(vf[kb][u], pk[kb][u], acc[m]);
     }
   }
 
@@ -474,18 +483,14 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int j, unsigned char*
   unsigned char* kpool = const_cast<unsigned char*>(static_cast<const unsigned char*>(a.kc));
   unsigned char* vpool = const_cast<unsigned char*>(static_cast<const unsigned char*>(a.vc));
   u32x4_t kreg[LOADS], vreg[LOADS];
+  auto page_rsrc = [&](unsigned char* pool, int k0, int pidx) {
+    const int idx = (k0 >> 4) + pidx;
+    const int id = btrow[min(idx, last_page)];
+    const bool ok = idx <= last_page && static_cast<unsigned>(id) < static_cast<unsigned>(a.num_blocks);
+    return __builtin_amdgcn_make_buffer_rsrc(pool + static_cast<size_t>(ok ? id : 0) * page_bytes, 0,
+                                             ok ? static_cast<int>(page_bytes) : 0, kRawBufferWord3);
+  };
   auto issue_tile = [&](int k0) {
-    __amdgpu_buffer_rsrc_t kr[BN / 16], vr[BN / 16];
-#pragma unroll
-    for (int pp = 0; pp < BN / 16; ++pp) {
-      const int idx = (k0 >> 4) + pp;
-      const int id = btrow[min(idx, last_page)];
-      const bool ok = idx <= last_page && static_cast<unsigned>(id) < static_cast<unsigned>(a.num_blocks);
-      const size_t base = static_cast<size_t>(ok ? id : 0) * page_bytes;
-      const int n = ok ? static_cast<int>(page_bytes) : 0;
-      kr[pp] = __builtin_amdgcn_make_buffer_rsrc(kpool + base, 0, n, kRawBufferWord3);
-      vr[pp] = __builtin_amdgcn_make_buffer_rsrc(vpool + base, 0, n, kRawBufferWord3);
-    }
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
       const int key = (it * kThreads + tid) / CPR;
@@ -493,8 +498,10 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int j, unsigned char*
       const uint32_t off = (k0 + key < kend)
                                ? (key & 15) * slot_bytes + head_off + (tid % CPR) * 16
                                : kOffsetOutOfRange;
-      kreg[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(kr[pidx], off, 0, 0));
-      vreg[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vr[pidx], off, 0, 0));
+      const auto kr = page_rsrc(kpool, k0, pidx);
+      const auto vr = page_rsrc(vpool, k0, pidx);
+      kreg[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
+      vreg[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0));
     }
   };
 
@@ -960,43 +967,80 @@ __device__ void decode_item_bf16(const MainArgs& a, int seg, int j, int split_ke
 }
 
 // ---------------------------------------------------------------- persistent kernel
+constexpr int kLdsSegments = 1024;  // item prefix sums of up to this many segments live in LDS
+
+__device__ __forceinline__ int find_segment_lds(const int* prefix, int n, int x) {
+  int lo = 0, hi = n;  // invariant: prefix[lo] <= x < prefix[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
   constexpr int kSmem = ChunkCfg<T>::template Sizes<D>::BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kSmem];
+  __shared__ int s_prefix[2][kLdsSegments + 1];
   __shared__ int s_work[3];
   const int n_chunk = a.hdr->n_chunk_items;
   const int n_dec = a.hdr->n_dec_items;
   const int n_total = n_chunk + n_dec;
   const int split_keys = a.hdr->split;
-  // Two queues: the first half of the workgroups takes chunk tiles while any
-  // are left, the second half decode splits; each falls back to the other
-  // queue when its own is empty.  Both roles therefore run side by side on
-  // every CU from the start of the launch.
-  const bool chunk_first = blockIdx.x < (gridDim.x + 1) / 2;
-  bool chunk_open = true, dec_open = true;  // meaningful in thread 0 only
+  const bool lds_lookup = a.num_seqs <= kLdsSegments;
+  if (lds_lookup) {
+    for (int i = threadIdx.x; i <= a.num_seqs; i += kThreads) {
+      s_prefix[0][i] = a.chunk_prefix[i];
+      s_prefix[1][i] = a.dec_prefix[i];
+    }
+  }
+  // Work distribution.  Two queues: the first half of the workgroups takes
+  // chunk tiles while any are left, the second half decode splits; each falls
+  // back to the other queue when its own is empty, so both roles run side by
+  // side on every CU.  The first item of every workgroup is assigned
+  // statically (the planner starts the counters past those items); afterwards
+  // the next item is claimed with an atomic at the start of the current one,
+  // so the claim's latency hides behind the work.
+  const int half = (gridDim.x + 1) / 2;
+  const bool chunk_first = blockIdx.x < half;
+  bool chunk_open = true, dec_open = true;  // used by thread 0 only
+  auto claim = [&]() -> int {
+    for (int attempt = 0; attempt < 2; ++attempt) {
+      const bool want_chunk = (attempt == 0) == chunk_first;
+      if (want_chunk && chunk_open) {
+        const int c = static_cast<int>(atomicAdd(&a.hdr->counter, 1u));
+        if (c < n_chunk) return c;
+        chunk_open = false;
+      } else if (!want_chunk && dec_open) {
+        const int d = static_cast<int>(atomicAdd(&a.hdr->dec_counter, 1u));
+        if (d < n_dec) return n_chunk + d;
+        dec_open = false;
+      }
+    }
+    return n_total;
+  };
+  int cur = n_total;
+  if (threadIdx.x == 0) {
+    if (chunk_first && static_cast<int>(blockIdx.x) < n_chunk) cur = blockIdx.x;
+    else if (!chunk_first && static_cast<int>(blockIdx.x) - half < n_dec) cur = n_chunk + blockIdx.x - half;
+    else cur = claim();
+  }
+  __syncthreads();  // LDS prefix copy complete
   for (;;) {
     if (threadIdx.x == 0) {
-      int it = n_total;
-      for (int attempt = 0; attempt < 2 && it == n_total; ++attempt) {
-        const bool want_chunk = (attempt == 0) == chunk_first;
-        if (want_chunk && chunk_open) {
-          const int c = static_cast<int>(atomicAdd(&a.hdr->counter, 1u));
-          if (c < n_chunk) it = c; else chunk_open = false;
-        } else if (!want_chunk && dec_open) {
-          const int d = static_cast<int>(atomicAdd(&a.hdr->dec_counter, 1u));
-          if (d < n_dec) it = n_chunk + d; else dec_open = false;
-        }
-      }
       int seg = 0, local = 0;
-      if (it < n_chunk) {
-        seg = find_segment(a.chunk_prefix, a.num_seqs, it);
-        local = it - a.chunk_prefix[seg];
-      } else if (it < n_total) {
-        seg = find_segment(a.dec_prefix, a.num_seqs, it - n_chunk);
-        local = it - n_chunk - a.dec_prefix[seg];
+      if (cur < n_chunk) {
+        seg = lds_lookup ? find_segment_lds(s_prefix[0], a.num_seqs, cur)
+                         : find_segment(a.chunk_prefix, a.num_seqs, cur);
+        local = cur - (lds_lookup ? s_prefix[0][seg] : a.chunk_prefix[seg]);
+      } else if (cur < n_total) {
+        const int d = cur - n_chunk;
+        seg = lds_lookup ? find_segment_lds(s_prefix[1], a.num_seqs, d)
+                         : find_segment(a.dec_prefix, a.num_seqs, d);
+        local = d - (lds_lookup ? s_prefix[1][seg] : a.dec_prefix[seg]);
       }
-      s_work[0] = it;
+      s_work[0] = cur;
       s_work[1] = seg;
       s_work[2] = local;
     }
@@ -1008,6 +1052,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
     const int local = __builtin_amdgcn_readfirstlane(s_work[2]);
     __syncthreads();
     if (it >= n_total) break;
+    if (threadIdx.x == 0) cur = claim();  // next item, claimed while this one runs
     if (it < n_chunk) {
       if constexpr (sizeof(T) == 2) chunk_tile_bf16<D>(a, seg, local, smem);
       else chunk_tile_f32<D>(a, seg, local, smem);
@@ -1098,7 +1143,7 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dt, int di) {
 
   PlanArgs pa{L.cu_seqlens_q, L.seqlens_k, L.num_seqs, L.total_q, L.max_seqlen_q, L.max_seqlen_k,
               L.max_blocks, L.num_heads, head_groups, L.ws.parts_cap, grid * kItemsPerSlot,
-              hdr, chunk_prefix, dec_prefix, part_prefix};
+              grid, hdr, chunk_prefix, dec_prefix, part_prefix};
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, L.stream, pa);
 
   MainArgs ma{L.q, L.k_cache, L.v_cache, L.out, L.cu_seqlens_q, L.seqlens_k, L.block_table,

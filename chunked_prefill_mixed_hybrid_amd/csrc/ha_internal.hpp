@@ -15,7 +15,7 @@ constexpr int kChunkRows = 128;     // query rows per chunk tile (32 per wave)
 constexpr int kSplitMin = 256;      // smallest decode KV split, in keys
 constexpr int kSplitCandidates = 23;  // decode split sizes kSplitMin << k, k < 23 (up to 2^30)
 constexpr int kPartsMax = 16384;    // cap on (segment, split) partial slots
-constexpr int kItemsPerSlot = 8;    // decode work items aimed at per resident workgroup
+constexpr int kItemsPerSlot = 16;   // decode work items aimed at per resident workgroup
 constexpr int kHeadsPerDecodeItem = 4;  // one head per wave
 constexpr int kMaxSeqlenK = 1 << 30;
 
