@@ -219,13 +219,18 @@ __device__ __forceinline__ int key_perm(int r) {
   return ((r >> 4) << 4) | (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 2) | (r & 3);
 }
 
+// XOR swizzle (in 16-byte chunks of 8 keys) of row d of the transposed V tile.
+__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
+constexpr uint32_t kBf16PairOne = 0x3f803f80u;  // (1.0, 1.0) as a bf16 pair
+
 template <typename T> struct ChunkCfg;
 template <> struct ChunkCfg<bf16_t> {
   template <int D> struct Sizes {
     static constexpr int BN = 64;
     static constexpr int KROW = (D + 8) * 2;   // bytes per key row of the K tile
-    static constexpr int VROW = (BN + 8) * 2;  // bytes per channel row of V^T
-    static constexpr int BYTES = BN * KROW + D * VROW;
+    static constexpr int VROW = BN * 2;        // bytes per channel row of V^T (swizzled, no pad)
+    static constexpr int STAGE = BN * KROW + D * VROW;
+    static constexpr int BYTES = 2 * STAGE;    // double buffered
   };
 };
 template <> struct ChunkCfg<float> {
@@ -241,13 +246,11 @@ template <int D>
 __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int j, unsigned char* smem) {
   using Cfg = ChunkCfg<bf16_t>::Sizes<D>;
   constexpr int BN = Cfg::BN, NKB = BN / 32, KS = D / 16, NM = D / 32;
-  constexpr int KROW = Cfg::KROW, VROW = Cfg::VROW;
-  constexpr int CPR = D * 2 / 16;            // 16-byte chunks per key row
+  constexpr int KROW = Cfg::KROW, VROW = Cfg::VROW, STAGE = Cfg::STAGE;
+  constexpr int CPR = D * 2 / 16;              // 16-byte chunks per key row
   constexpr int KLOADS = BN * CPR / kThreads;  // K chunks per thread per tile
   constexpr int VKG = BN * CPR / kThreads;     // keys per thread in the V transpose
   static_assert(KLOADS * kThreads == BN * CPR, "tile load must divide evenly");
-  unsigned char* Ks = smem;
-  unsigned char* Vt = smem + BN * KROW;
 
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int qc = lane & 31, g = lane >> 5;
@@ -279,11 +282,10 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int j, unsigned char
   float m_run = -INFINITY, l_run = 0.f;
 
   // Tile loads.  Every 16-byte load of a tile reads from one page that is the
-  // same for the whole wave (K: load `it` covers page it (D=128) or
-  // 2*it + w/2 (D=64); V: wave w covers page w), so the pages are scalar
-  // loads from the block table and the gathers are buffer loads with a
-  // 32-bit lane offset.  Keys at or past kend read as zero (offset out of
-  // range, or an empty descriptor for whole pages).
+  // same for the whole wave (K load `it`: page (it*256 + 64w) / (16*CPR) of the
+  // tile; V: page w), so page ids are scalar block-table reads and the gathers
+  // are buffer loads with a 32-bit lane offset.  Keys at or past kend read as
+  // zero (offset out of range, or an empty descriptor for whole pages).
   const_i32_t* btrow = (const_i32_t*)(a.bt) + static_cast<size_t>(seg) * a.max_blocks;
   const int last_page = (kend - 1) >> 4;
   const uint32_t slot_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 2;
@@ -293,26 +295,32 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int j, unsigned char
   unsigned char* vpool = const_cast<unsigned char*>(static_cast<const unsigned char*>(a.vc));
   const int vc_ = tid % CPR, vkg = tid / CPR;  // V transpose: chunk and key group of this thread
   u32x4_t kreg[KLOADS], vreg[VKG];
-  // Descriptor of page `pidx` of the tile starting at key k0 (uniform pidx);
-  // empty past kend or for a block id outside the pool.
-  auto page_rsrc = [&](unsigned char* pool, int k0, int pidx) {
-    const int idx = (k0 >> 4) + pidx;
-    const int id = btrow[min(idx, last_page)];
-    const bool ok = idx <= last_page && static_cast<unsigned>(id) < static_cast<unsigned>(a.num_blocks);
-    return __builtin_amdgcn_make_buffer_rsrc(pool + static_cast<size_t>(ok ? id : 0) * page_bytes, 0,
-                                             ok ? static_cast<int>(page_bytes) : 0, kRawBufferWord3);
+  // page ids of a tile (scalar loads); -1 past kend or outside the pool
+  auto tile_ids = [&](int k0, int (&ids)[4]) {
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const int idx = (k0 >> 4) + pp;
+      const int id = btrow[min(idx, last_page)];
+      ids[pp] = (idx <= last_page && static_cast<unsigned>(id) < static_cast<unsigned>(a.num_blocks)) ? id : -1;
+    }
   };
-  auto issue_tile = [&](int k0) {
+  auto issue_tile = [&](int k0, const int (&ids)[4]) {
+    auto rsrc = [&](unsigned char* pool, int pidx) {  // pidx uniform: select, no indexed array
+      const int id = pidx == 0 ? ids[0] : pidx == 1 ? ids[1] : pidx == 2 ? ids[2] : ids[3];
+      return __builtin_amdgcn_make_buffer_rsrc(pool + static_cast<size_t>(id < 0 ? 0 : id) * page_bytes,
+                                               0, id < 0 ? 0 : static_cast<int>(page_bytes),
+                                               kRawBufferWord3);
+    };
 #pragma unroll
     for (int it = 0; it < KLOADS; ++it) {
       const int key = (it * kThreads + tid) / CPR;
       const uint32_t off = (k0 + key < kend)
                                ? (key & 15) * slot_bytes + head_off + (tid % CPR) * 16
                                : kOffsetOutOfRange;
-      const auto rs = page_rsrc(kpool, k0, (it * kThreads + w * kWave) / (16 * CPR));
+      const auto rs = rsrc(kpool, (it * kThreads + w * kWave) / (16 * CPR));
       kreg[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
     }
-    const auto rs = page_rsrc(vpool, k0, w);  // V keys of wave w all sit in page w of the tile
+    const auto rs = rsrc(vpool, w);
 #pragma unroll
     for (int t = 0; t < VKG; ++t) {
       const int key = vkg * VKG + t;
@@ -322,17 +330,17 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int j, unsigned char
       vreg[t] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
     }
   };
-
-  issue_tile(0);
-  for (int k0 = 0; k0 < kend; k0 += BN) {
-    __syncthreads();  // previous tile fully consumed
-    // K tile, natural layout Ks[key][d]
+  // Registers -> one LDS stage: K natural Ks[key][d]; V transposed Vt[d][key]
+  // with 128-byte rows whose 16-byte chunks (8 keys) are XOR-swizzled by
+  // vt_swz(d): the transposed writes (16 lanes on rows 8 apart) and the MFMA
+  // operand reads (32 consecutive rows) then spread over all LDS banks.
+  auto store_tile = [&](unsigned char* st) {
 #pragma unroll
     for (int it = 0; it < KLOADS; ++it) {
       const int idx = it * kThreads + tid;
-      st16(Ks + (idx / CPR) * KROW + (idx % CPR) * 16, kreg[it]);
+      st16(st + (idx / CPR) * KROW + (idx % CPR) * 16, kreg[it]);
     }
-    // V tile, transposed: Vt[d][key]; thread owns chunk vc_ (8 channels) of VKG keys
+    unsigned char* vt = st + BN * KROW;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       uint32_t hv[VKG];
@@ -341,7 +349,8 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int j, unsigned char
         const uint32_t word = vreg[t][e >> 1];
         hv[t] = (e & 1) ? (word >> 16) : (word & 0xffffu);
       }
-      unsigned char* dst = Vt + (vc_ * 8 + e) * VROW + vkg * VKG * 2;
+      const int d = vc_ * 8 + e;
+      unsigned char* dst = vt + d * VROW + (((vkg * VKG) >> 3) ^ vt_swz(d)) * 16 + ((vkg * VKG) & 7) * 2;
       if constexpr (VKG == 4) {
         st8(dst, u32x2_t{hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)});
       } else {
@@ -349,75 +358,108 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int j, unsigned char
         *reinterpret_cast<uint32_t*>(dst) = hv[0] | (hv[1] << 16);
       }
     }
-    __syncthreads();
-    issue_tile(k0 + BN);  // next tile streams in while this one is computed
-    if (!wave_active || k0 > H0 + wrow0 + 31) continue;  // tile invisible to this wave
-    const bool need_mask = (k0 + BN - 1) > (H0 + wrow0);
+  };
 
-    // S^T = K Q^T, two 32-key blocks
-    f32x16_t sacc[NKB];
+  // Two LDS stages: while tile i is computed from one stage, tile i+1 is
+  // written into the other and tile i+2 streams into registers; one barrier
+  // per tile.
+  int ids_a[4], ids_b[4];
+  tile_ids(0, ids_a);
+  issue_tile(0, ids_a);
+  tile_ids(BN, ids_b);
+  store_tile(smem);
+  issue_tile(BN, ids_b);
+  tile_ids(2 * BN, ids_a);  // ids are read one tile ahead of their loads
+  __syncthreads();
+  for (int k0 = 0, i = 0; k0 < kend; k0 += BN, ++i) {
+    const unsigned char* Ks = smem + (i & 1) * STAGE;
+    const unsigned char* Vt = Ks + BN * KROW;
+    if (wave_active && k0 <= H0 + wrow0 + 31) {  // else the tile is invisible to this wave
+      const bool need_mask = (k0 + BN - 1) > (H0 + wrow0);
+      // S^T = K Q^T, two 32-key blocks
+      // the two 32-key blocks accumulate independently: interleave their MFMAs so
+      // the matrix pipe never waits on the previous accumulator of one chain
+      f32x16_t sacc[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      sacc[kb] = f32x16_t{};
-      const unsigned char* kr = Ks + (kb * 32 + pi) * KROW + g * 16;
-      u32x4_t kf[KS];  // all K fragments of the block first, then the MFMA chain
+      for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16_t{};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kf[s] = ld16(kr + s * 32);
+      for (int s = 0; s < KS; s += 2) {
+        u32x4_t kf[NKB][2];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) sacc[kb] = mfma_bf16(kf[s], qf[s], sacc[kb]);
-    }
-    // scale (base 2), causal mask on diagonal tiles, running max
-    float tmax = -INFINITY;
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+          for (int t = 0; t < 2; ++t) kf[kb][t] = ld16(Ks + (kb * 32 + pi) * KROW + g * 16 + (s + t) * 32);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float x = sacc[kb][v] * a.scale_log2;
-        if (need_mask) {
-          const int kp = k0 + kb * 32 + ((v >> 3) << 4) + (g << 3) + (v & 7);
-          if (kp > H0 + my_row) x = -INFINITY;
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) sacc[kb] = mfma_bf16(kf[kb][t], qf[s + t], sacc[kb]);
+      }
+      // causal mask on diagonal tiles, running max of the raw scores (the
+      // positive scale preserves order), weights exp2(scale * (s - max))
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float x = sacc[kb][v];
+          if (need_mask) {
+            const int kp = k0 + kb * 32 + ((v >> 3) << 4) + (g << 3) + (v & 7);
+            if (kp > H0 + my_row) x = -INFINITY;
+          }
+          sacc[kb][v] = x;
+          tmax = fmaxf(tmax, x);
         }
-        sacc[kb][v] = x;
-        tmax = fmaxf(tmax, x);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m_run, tmax);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2((m_run - m_use) * a.scale_log2);
+      const float neg_m = -m_use * a.scale_log2;
+      m_run = m_new;
+      float psum = 0.f;
+      u32x4_t pk[NKB][2];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const float p0 = fast_exp2(fmaf(sacc[kb][8 * u + 2 * e2], a.scale_log2, neg_m));
+            const float p1 = fast_exp2(fmaf(sacc[kb][8 * u + 2 * e2 + 1], a.scale_log2, neg_m));
+            const uint32_t w2 = pack_bf16x2(p0, p1);
+            pk[kb][u][e2] = w2;
+            psum = dot2_bf16(w2, kBf16PairOne, psum);  // the same rounded weights P.V uses
+          }
+        }
+      }
+      l_run = l_run * alpha + psum;
+      if (__any(alpha != 1.f)) {  // no row max moved: the accumulators need no rescale
+#pragma unroll
+        for (int m = 0; m < NM; ++m) acc[m] *= alpha;
+      }
+      // O^T += V^T P^T: for each 16-key slice, the NM channel blocks are
+      // independent accumulators, issued back to back
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          u32x4_t vf[NM];
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            const int d = m * 32 + qc;
+            vf[m] = ld16(Vt + d * VROW + ((kb * 4 + u * 2 + g) ^ vt_swz(d)) * 16);
+          }
+#pragma unroll
+          for (int m = 0; m < NM; ++m) acc[m] = mfma_bf16(vf[m], pk[kb][u], acc[m]);
+        }
       }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    float psum = 0.f;
-    u32x4_t pk[NKB][2];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const float p0 = fast_exp2(sacc[kb][8 * u + 2 * e2] - m_use);
-          const float p1 = fast_exp2(sacc[kb][8 * u + 2 * e2 + 1] - m_use);
-          psum += p0 + p1;
-          pk[kb][u][e2] = pack_bf16x2(p0, p1);
-        }
-      }
+    if (k0 + BN < kend) {
+      store_tile(smem + ((i + 1) & 1) * STAGE);  // tile i+1, loaded during tile i
+      issue_tile(k0 + 2 * BN, ids_a);           // tile i+2 streams in
+      tile_ids(k0 + 3 * BN, ids_a);
     }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int m = 0; m < NM; ++m) acc[m] *= alpha;
-    // O^T += V^T P^T
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const unsigned char* vr = Vt + (m * 32 + qc) * VROW + g * 16;
-      u32x4_t vf[NKB][2];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) vf[kb][u] = ld16(vr + (kb * 32 + u * 16) * 2);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) acc[m] = mfma_bf16(vf[kb][u], pk[kb][u], acc[m]);
-    }
+    __syncthreads();
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);  // lanes l and l^32 share a row
@@ -967,7 +1009,7 @@ __device__ void decode_item_bf16(const MainArgs& a, int seg, int j, int split_ke
 }
 
 // ---------------------------------------------------------------- persistent kernel
-constexpr int kLdsSegments = 1024;  // item prefix sums of up to this many segments live in LDS
+constexpr int kLdsSegments = 512;  // item prefix sums of up to this many segments live in LDS
 
 __device__ __forceinline__ int find_segment_lds(const int* prefix, int n, int x) {
   int lo = 0, hi = n;  // invariant: prefix[lo] <= x < prefix[hi]
@@ -1088,17 +1130,27 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(MainArgs a) {
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
   for (int s0 = 0; s0 < np; s0 += kWave) {
     const int sp = s0 + lane;
-    float wgt = 0.f;
+    float wgt = 0.f;  // weight of split s0 + lane (0 past the last split)
     if (sp < np) {
       wgt = fast_exp2(base[sp * step] - mx);
       l = fmaf(base[sp * step + 1], wgt, l);
     }
     const int n = min(kWave, np - s0);
-    for (int t = 0; t < n; ++t) {
-      const float wt = __shfl(wgt, t);
-      const float* pp = base + (s0 + t) * step + 4 + lane * EPL;
+    for (int t0 = 0; t0 < n; t0 += 8) {  // 8 independent partial loads in flight
+      float v[8][EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[e] = fmaf(pp[e], wt, o[e]);
+      for (int jj = 0; jj < 8; ++jj) {
+        const int t = t0 + jj;
+        const float* pp = base + (s0 + min(t, n - 1)) * step + 4 + lane * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) v[jj][e] = pp[e];
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const float wt = t0 + jj < n ? __shfl(wgt, t0 + jj) : 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[e] = fmaf(v[jj][e], wt, o[e]);
+      }
     }
   }
   const float inv = 1.f / wave_sum(l);
