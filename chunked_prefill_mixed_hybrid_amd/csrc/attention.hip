@@ -42,7 +42,7 @@ struct PlanArgs {
   int num_seqs, total_q, max_q, max_k, max_blocks, num_heads, head_groups, parts_cap,
       target_items, grid;
   PlanHeader* hdr;
-  int32_t* chunk_prefix;
+  int32_t* tile_prefix;
   int32_t* dec_prefix;
   int32_t* part_prefix;
 };
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __syncthreads();
   const int split = kSplitMin << s_split_log;
 
-  // 2. exclusive prefix sums of chunk items, decode items and partial slots.
+  // 2. exclusive prefix sums of chunk tiles, decode items and partial slots.
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   for (int base = 0; base < a.num_seqs; base += kPlanThreads) {
     const int b = base + tid;
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       if (!plan_segment(a, b, lq, lk)) {
         atomicAdd(&s_bad, 1);
       } else if (lq >= 2) {
-        v[0] = ((lq + kChunkRows - 1) / kChunkRows) * a.num_heads;
+        v[0] = (lq + kChunkRows - 1) / kChunkRows;  // query tiles (per head)
       } else if (lq == 1) {
         const int n = (lk + split - 1) / split;
         v[1] = n * a.head_groups;
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     }
     __syncthreads();
     if (b < a.num_seqs) {
-      a.chunk_prefix[b] = s_carry[0] + s_wave_tot[wave][0] + incl[0] - v[0];
+      a.tile_prefix[b] = s_carry[0] + s_wave_tot[wave][0] + incl[0] - v[0];
       a.dec_prefix[b] = s_carry[1] + s_wave_tot[wave][1] + incl[1] - v[1];
       a.part_prefix[b] = s_carry[2] + s_wave_tot[wave][2] + incl[2] - v[2];
     }
@@ -164,18 +164,23 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     __syncthreads();
   }
   if (tid == 0) {
-    a.chunk_prefix[a.num_seqs] = s_carry[0];
+    a.tile_prefix[a.num_seqs] = s_carry[0];
     a.dec_prefix[a.num_seqs] = s_carry[1];
     a.part_prefix[a.num_seqs] = s_carry[2];
-    a.hdr->n_chunk_items = s_carry[0];
+    a.hdr->n_chunk_tiles = s_carry[0];
     a.hdr->n_dec_items = s_carry[1];
     a.hdr->n_parts = s_carry[2];
     a.hdr->split = split;
     a.hdr->bad_segments = s_bad;
     // the attention kernel hands out the first item of every workgroup statically:
-    // chunk items [0, half) to the first half, decode items [0, grid - half) to the rest
+    // chunk-first workgroup b takes item b / 8 of chunk group b % 8, decode-first
+    // workgroup b takes decode item b - half; the counters start past those items
     const int half = (a.grid + 1) / 2;
-    a.hdr->counter = static_cast<uint32_t>(min(s_carry[0], half));
+    for (int x = 0; x < kXcdGroups; ++x) {
+      const int items = chunk_group_heads(a.num_heads, x) * s_carry[0];
+      const int first = x < half ? (half - x + kXcdGroups - 1) / kXcdGroups : 0;
+      a.hdr->chunk_counter[x] = static_cast<uint32_t>(min(items, first));
+    }
     a.hdr->dec_counter = static_cast<uint32_t>(min(s_carry[1], a.grid - half));
   }
 }
@@ -192,7 +197,7 @@ struct MainArgs {
   int num_seqs, num_heads, num_kv_heads, group, num_blocks, max_blocks, part_stride;
   float scale_log2;  // sm_scale * log2(e): softmax runs in base 2
   PlanHeader* hdr;
-  const int32_t* chunk_prefix;
+  const int32_t* tile_prefix;
   const int32_t* dec_prefix;
   const int32_t* part_prefix;
   float* partials;
@@ -243,7 +248,7 @@ template <> struct ChunkCfg<float> {
 
 // ---------------------------------------------------------------- chunk role, bf16
 template <int D>
-__device__ void chunk_tile_bf16(const MainArgs& a, int seg, int j, unsigned char* smem) {
+__device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, unsigned char* smem) {
   using Cfg = ChunkCfg<bf16_t>::Sizes<D>;
   constexpr int BN = Cfg::BN, NKB = BN / 32, KS = D / 16, NM = D / 32;
   constexpr int KROW = Cfg::KROW, VROW = Cfg::VROW, STAGE = Cfg::STAGE;
@@ -255,8 +260,6 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int j, unsigned char
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int qc = lane & 31, g = lane >> 5;
   const int q0 = a.cu[seg], Lq = a.cu[seg + 1] - q0, Lk = a.sk[seg], H0 = Lk - Lq;
-  const int ntiles = (Lq + kChunkRows - 1) / kChunkRows;
-  const int h = j / ntiles, tile = ntiles - 1 - (j - h * ntiles);
   const int kvh = h / a.group;
   const int row0 = tile * kChunkRows;
   const int rows_end = min(row0 + kChunkRows, Lq);
@@ -479,7 +482,7 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int j, unsigned char
 
 // ---------------------------------------------------------------- chunk role, fp32
 template <int D>
-__device__ void chunk_tile_f32(const MainArgs& a, int seg, int j, unsigned char* smem) {
+__device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, unsigned char* smem) {
   using Cfg = ChunkCfg<float>::Sizes<D>;
   constexpr int BN = Cfg::BN, NKB = BN / 32, KS = D / 2, NM = D / 32, ROWF = Cfg::ROWF;
   constexpr int CPR = D / 4;
@@ -491,8 +494,6 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int j, unsigned char*
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int qc = lane & 31, g = lane >> 5;
   const int q0 = a.cu[seg], Lq = a.cu[seg + 1] - q0, Lk = a.sk[seg], H0 = Lk - Lq;
-  const int ntiles = (Lq + kChunkRows - 1) / kChunkRows;
-  const int h = j / ntiles, tile = ntiles - 1 - (j - h * ntiles);
   const int kvh = h / a.group;
   const int row0 = tile * kChunkRows;
   const int rows_end = min(row0 + kChunkRows, Lq);
@@ -1025,82 +1026,131 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
   constexpr int kSmem = ChunkCfg<T>::template Sizes<D>::BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kSmem];
   __shared__ int s_prefix[2][kLdsSegments + 1];
-  __shared__ int s_work[3];
-  const int n_chunk = a.hdr->n_chunk_items;
+  __shared__ int s_work[4];
+  // scheduler state, touched by thread 0 only; kept in LDS so no register holds
+  // it across work items
+  __shared__ int s_next;           // item claimed for the next iteration
+  __shared__ unsigned s_chunk_open;  // bit x: chunk group x may still have items
+  __shared__ int s_dec_open;
+  const int n_tiles = a.hdr->n_chunk_tiles;
   const int n_dec = a.hdr->n_dec_items;
-  const int n_total = n_chunk + n_dec;
   const int split_keys = a.hdr->split;
   const bool lds_lookup = a.num_seqs <= kLdsSegments;
   if (lds_lookup) {
     for (int i = threadIdx.x; i <= a.num_seqs; i += kThreads) {
-      s_prefix[0][i] = a.chunk_prefix[i];
+      s_prefix[0][i] = a.tile_prefix[i];
       s_prefix[1][i] = a.dec_prefix[i];
     }
   }
-  // Work distribution.  Two queues: the first half of the workgroups takes
-  // chunk tiles while any are left, the second half decode splits; each falls
-  // back to the other queue when its own is empty, so both roles run side by
-  // side on every CU.  The first item of every workgroup is assigned
-  // statically (the planner starts the counters past those items); afterwards
-  // the next item is claimed with an atomic at the start of the current one,
-  // so the claim's latency hides behind the work.
+  // Work distribution.  Decode splits come from one queue; chunk tiles from
+  // kXcdGroups queues (tiles of head h in group h % kXcdGroups).  The first half
+  // of the workgroups takes chunk tiles while any are left -- its own XCD's group
+  // first, then the others -- the second half decode splits; each falls back to
+  // the other kind when its own is empty, so both roles run side by side on every
+  // CU.  The first item of every workgroup is assigned statically (the planner
+  // starts the counters past those items); afterwards the next item is claimed
+  // with an atomic at the start of the current one, hiding the claim's latency.
+  // Item codes: chunk (group x, index i) = x << 24 | i; decode d = kDecodeTag | d.
+  constexpr int kDecodeTag = 1 << 28, kDone = 0x7fffffff;
   const int half = (gridDim.x + 1) / 2;
   const bool chunk_first = blockIdx.x < half;
-  bool chunk_open = true, dec_open = true;  // used by thread 0 only
-  auto claim = [&]() -> int {
-    for (int attempt = 0; attempt < 2; ++attempt) {
-      const bool want_chunk = (attempt == 0) == chunk_first;
-      if (want_chunk && chunk_open) {
-        const int c = static_cast<int>(atomicAdd(&a.hdr->counter, 1u));
-        if (c < n_chunk) return c;
-        chunk_open = false;
-      } else if (!want_chunk && dec_open) {
-        const int d = static_cast<int>(atomicAdd(&a.hdr->dec_counter, 1u));
-        if (d < n_dec) return n_chunk + d;
-        dec_open = false;
+  const int my_group = blockIdx.x % kXcdGroups;
+  auto claim_chunk = [&]() -> int {
+    if (!s_chunk_open) return kDone;
+    // one round of independent (relaxed, device-scope) counter reads closes the
+    // groups already drained, so at most one atomic is spent on a likely winner
+    // instead of a chain of failing atomics
+    unsigned seen[kXcdGroups];
+#pragma unroll
+    for (int x = 0; x < kXcdGroups; ++x)
+      seen[x] = __hip_atomic_load(&a.hdr->chunk_counter[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned open = s_chunk_open;
+#pragma unroll
+    for (int x = 0; x < kXcdGroups; ++x)
+      if (seen[x] >= static_cast<unsigned>(chunk_group_heads(a.num_heads, x) * n_tiles)) open &= ~(1u << x);
+    for (int k = 0; k < kXcdGroups && open; ++k) {
+      const int x = (my_group + k) % kXcdGroups;
+      if (!(open & (1u << x))) continue;
+      const int n = chunk_group_heads(a.num_heads, x) * n_tiles;
+      const int c = static_cast<int>(atomicAdd(&a.hdr->chunk_counter[x], 1u));
+      if (c < n) {
+        s_chunk_open = open;
+        return (x << 24) | c;
       }
+      open &= ~(1u << x);
     }
-    return n_total;
+    s_chunk_open = open;
+    return kDone;
   };
-  int cur = n_total;
+  auto claim_dec = [&]() -> int {
+    if (!s_dec_open) return kDone;
+    const int d = static_cast<int>(atomicAdd(&a.hdr->dec_counter, 1u));
+    if (d < n_dec) return kDecodeTag | d;
+    s_dec_open = 0;
+    return kDone;
+  };
+  auto claim = [&]() -> int {
+    int it = chunk_first ? claim_chunk() : claim_dec();
+    if (it == kDone) it = chunk_first ? claim_dec() : claim_chunk();
+    return it;
+  };
   if (threadIdx.x == 0) {
-    if (chunk_first && static_cast<int>(blockIdx.x) < n_chunk) cur = blockIdx.x;
-    else if (!chunk_first && static_cast<int>(blockIdx.x) - half < n_dec) cur = n_chunk + blockIdx.x - half;
-    else cur = claim();
+    s_chunk_open = (1u << kXcdGroups) - 1;
+    s_dec_open = 1;
+    const int rank = blockIdx.x / kXcdGroups;  // among chunk-first workgroups of this group
+    if (chunk_first && rank < chunk_group_heads(a.num_heads, my_group) * n_tiles)
+      s_next = (my_group << 24) | rank;
+    else if (!chunk_first && static_cast<int>(blockIdx.x) - half < n_dec)
+      s_next = kDecodeTag | (blockIdx.x - half);
+    else
+      s_next = claim();
   }
   __syncthreads();  // LDS prefix copy complete
   for (;;) {
     if (threadIdx.x == 0) {
-      int seg = 0, local = 0;
-      if (cur < n_chunk) {
-        seg = lds_lookup ? find_segment_lds(s_prefix[0], a.num_seqs, cur)
-                         : find_segment(a.chunk_prefix, a.num_seqs, cur);
-        local = cur - (lds_lookup ? s_prefix[0][seg] : a.chunk_prefix[seg]);
-      } else if (cur < n_total) {
-        const int d = cur - n_chunk;
+      const int cur = s_next;
+      int kind = 0, seg = 0, p1 = 0, p2 = 0;  // kind: 0 done, 1 chunk, 2 decode
+      if (cur != kDone && (cur & kDecodeTag)) {
+        const int d = cur & (kDecodeTag - 1);
         seg = lds_lookup ? find_segment_lds(s_prefix[1], a.num_seqs, d)
                          : find_segment(a.dec_prefix, a.num_seqs, d);
-        local = d - (lds_lookup ? s_prefix[1][seg] : a.dec_prefix[seg]);
+        p1 = d - (lds_lookup ? s_prefix[1][seg] : a.dec_prefix[seg]);
+        kind = 2;
+      } else if (cur != kDone) {
+        // group x holds, segment by segment, (head x + 8k, tile) for its heads
+        const int x = cur >> 24, i = cur & ((1 << 24) - 1);
+        const int nh = chunk_group_heads(a.num_heads, x);
+        const int t = i / nh;  // tile rank over all segments, scaled down by the group's heads
+        seg = lds_lookup ? find_segment_lds(s_prefix[0], a.num_seqs, t)
+                         : find_segment(a.tile_prefix, a.num_seqs, t);
+        const int t0 = lds_lookup ? s_prefix[0][seg] : a.tile_prefix[seg];
+        const int nt = (lds_lookup ? s_prefix[0][seg + 1] : a.tile_prefix[seg + 1]) - t0;
+        const int local = i - nh * t0;
+        p1 = x + kXcdGroups * (local / nt);   // query head
+        p2 = nt - 1 - local % nt;             // query tile, longest first
+        kind = 1;
       }
-      s_work[0] = cur;
+      s_work[0] = kind;
       s_work[1] = seg;
-      s_work[2] = local;
+      s_work[2] = p1;
+      s_work[3] = p2;
     }
     __syncthreads();
     // the work item is uniform across the workgroup: keep it in scalar registers so
     // every address derived from it (segment row, block-table row, pages) is scalar
-    const int it = __builtin_amdgcn_readfirstlane(s_work[0]);
+    const int kind = __builtin_amdgcn_readfirstlane(s_work[0]);
     const int seg = __builtin_amdgcn_readfirstlane(s_work[1]);
-    const int local = __builtin_amdgcn_readfirstlane(s_work[2]);
+    const int p1 = __builtin_amdgcn_readfirstlane(s_work[2]);
+    const int p2 = __builtin_amdgcn_readfirstlane(s_work[3]);
     __syncthreads();
-    if (it >= n_total) break;
-    if (threadIdx.x == 0) cur = claim();  // next item, claimed while this one runs
-    if (it < n_chunk) {
-      if constexpr (sizeof(T) == 2) chunk_tile_bf16<D>(a, seg, local, smem);
-      else chunk_tile_f32<D>(a, seg, local, smem);
+    if (kind == 0) break;
+    if (threadIdx.x == 0) s_next = claim();  // next item, claimed while this one runs
+    if (kind == 1) {
+      if constexpr (sizeof(T) == 2) chunk_tile_bf16<D>(a, seg, p1, p2, smem);
+      else chunk_tile_f32<D>(a, seg, p1, p2, smem);
     } else {
-      if constexpr (sizeof(T) == 2) decode_item_bf16<D>(a, seg, local, split_keys);
-      else decode_item<T, D>(a, seg, local, split_keys);
+      if constexpr (sizeof(T) == 2) decode_item_bf16<D>(a, seg, p1, split_keys);
+      else decode_item<T, D>(a, seg, p1, split_keys);
     }
   }
 }
@@ -1188,20 +1238,20 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dt, int di) {
   const int grid = info.cus * info.slots[dt][di];
   unsigned char* ws = L.workspace;
   PlanHeader* hdr = reinterpret_cast<PlanHeader*>(ws);
-  int32_t* chunk_prefix = reinterpret_cast<int32_t*>(ws + L.ws.chunk_prefix);
+  int32_t* tile_prefix = reinterpret_cast<int32_t*>(ws + L.ws.tile_prefix);
   int32_t* dec_prefix = reinterpret_cast<int32_t*>(ws + L.ws.dec_prefix);
   int32_t* part_prefix = reinterpret_cast<int32_t*>(ws + L.ws.part_prefix);
   const int head_groups = (L.num_heads + kHeadsPerDecodeItem - 1) / kHeadsPerDecodeItem;
 
   PlanArgs pa{L.cu_seqlens_q, L.seqlens_k, L.num_seqs, L.total_q, L.max_seqlen_q, L.max_seqlen_k,
               L.max_blocks, L.num_heads, head_groups, L.ws.parts_cap, grid * kItemsPerSlot,
-              grid, hdr, chunk_prefix, dec_prefix, part_prefix};
+              grid, hdr, tile_prefix, dec_prefix, part_prefix};
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, L.stream, pa);
 
   MainArgs ma{L.q, L.k_cache, L.v_cache, L.out, L.cu_seqlens_q, L.seqlens_k, L.block_table,
               L.num_seqs, L.num_heads, L.num_kv_heads, L.num_heads / L.num_kv_heads,
               L.num_blocks, L.max_blocks, L.ws.part_stride, L.sm_scale * kLog2e, hdr,
-              chunk_prefix, dec_prefix, part_prefix,
+              tile_prefix, dec_prefix, part_prefix,
               reinterpret_cast<float*>(ws + L.ws.partials)};
   hipLaunchKernelGGL((attn_kernel<T, D>), dim3(grid), dim3(kThreads), 0, L.stream, ma);
   hipLaunchKernelGGL((combine_kernel<T, D>), dim3(L.num_seqs * head_groups), dim3(kThreads), 0,

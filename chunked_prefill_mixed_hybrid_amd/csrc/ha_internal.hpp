@@ -20,24 +20,34 @@ constexpr int kHeadsPerDecodeItem = 4;  // one head per wave
 constexpr int kMaxSeqlenK = 1 << 30;
 
 // ---- workspace ---------------------------------------------------------------------
-// [header 256 B][chunk_prefix (B+1)][dec_prefix (B+1)][part_prefix (B+1)]
+// [header 256 B][tile_prefix (B+1)][dec_prefix (B+1)][part_prefix (B+1)]
 // [partials parts_cap x H x (D + 4) fp32]; every array starts on a 256-byte boundary.
+// Chunk tiles are queued in kXcdGroups groups: the tiles of query head h go to
+// group h % kXcdGroups, and workgroup b prefers group b % kXcdGroups.  Work-
+// groups are dispatched to the 8 XCDs of an MI355X round robin, so the query
+// tiles of one head run side by side on one XCD and re-read its KV history
+// from that XCD's L2 instead of HBM.
+constexpr int kXcdGroups = 8;
+__host__ __device__ inline int chunk_group_heads(int num_heads, int x) {
+  return num_heads / kXcdGroups + (x < num_heads % kXcdGroups ? 1 : 0);
+}
+
 struct PlanHeader {
-  uint32_t counter;       // next chunk-tile item (reset to 0 by the planner each call)
-  uint32_t dec_counter;   // next decode item (reset to 0 by the planner each call)
-  int32_t n_chunk_items;  // items [0, n_chunk_items) are chunk tiles
-  int32_t n_dec_items;    // items [n_chunk_items, +n_dec_items) are decode splits
+  uint32_t chunk_counter[kXcdGroups];  // next chunk item of each group (set by the planner)
+  uint32_t dec_counter;   // next decode item (set by the planner each call)
+  int32_t n_chunk_tiles;  // query tiles (per head) over all chunk segments
+  int32_t n_dec_items;    // decode (segment, split, 4-head group) items
   int32_t split;          // decode split size in keys (multiple of 64)
   int32_t n_parts;        // partial slots in use
   int32_t bad_segments;   // segments skipped because they broke a precondition
-  int32_t pad[57];
+  int32_t pad[50];
 };
 static_assert(sizeof(PlanHeader) == 256, "header is 256 bytes");
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t chunk_prefix, dec_prefix, part_prefix, partials, total;
+  size_t tile_prefix, dec_prefix, part_prefix, partials, total;
   int parts_cap;
   int part_stride;  // floats per (part, head): m, l, 2 pad, acc[D]
 };
@@ -52,7 +62,7 @@ inline WsLayout ws_layout(int num_seqs, int max_seqlen_k, int num_heads, int hea
   WsLayout l;
   size_t off = sizeof(PlanHeader);
   size_t arr = align256(sizeof(int32_t) * (static_cast<size_t>(num_seqs) + 1));
-  l.chunk_prefix = off; off += arr;
+  l.tile_prefix = off; off += arr;
   l.dec_prefix = off; off += arr;
   l.part_prefix = off; off += arr;
   l.parts_cap = parts_cap_for(num_seqs, max_seqlen_k);
