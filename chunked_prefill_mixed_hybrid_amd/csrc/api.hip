@@ -47,9 +47,8 @@ ha_status paged_kv_append(const void* key, const void* value, const int32_t* slo
 
 size_t hybrid_attn_workspace_size(int32_t num_seqs, int32_t total_q, int32_t max_seqlen_k,
                                   int32_t num_heads, int32_t head_dim) {
-  (void)total_q;
-  if (num_seqs < 1 || max_seqlen_k < 0 || num_heads < 1 || head_dim < 1) return 0;
-  return ha::ws_layout(num_seqs, max_seqlen_k, num_heads, head_dim).total;
+  if (num_seqs < 1 || total_q < 0 || max_seqlen_k < 0 || num_heads < 1 || head_dim < 1) return 0;
+  return ha::ws_layout(num_seqs, total_q, max_seqlen_k, num_heads, head_dim).total;
 }
 
 ha_status hybrid_attn_fwd(const void* q, const void* k_cache, const void* v_cache,
@@ -73,7 +72,7 @@ ha_status hybrid_attn_fwd(const void* q, const void* k_cache, const void* v_cach
     return HA_ERR_INVALID_ARGUMENT;
   if (total_q > 0 && (!q || !out)) return HA_ERR_INVALID_ARGUMENT;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return HA_ERR_INVALID_ARGUMENT;
-  const ha::WsLayout ws = ha::ws_layout(num_seqs, max_seqlen_k, num_heads, head_dim);
+  const ha::WsLayout ws = ha::ws_layout(num_seqs, total_q, max_seqlen_k, num_heads, head_dim);
   if (workspace_bytes < ws.total) return HA_ERR_WORKSPACE_TOO_SMALL;
   if (total_q == 0) return HA_OK;
 

@@ -40,7 +40,10 @@ struct PlanArgs {
   const int32_t* cu;
   const int32_t* sk;
   int num_seqs, total_q, max_q, max_k, max_blocks, num_heads, head_groups, parts_cap,
-      target_items, grid;
+      target_items, grid, tiles_cap, chunk_slots_cap;
+  // rough cost of one 64-key step of a chunk tile, in units of one decode
+  // (key, head) pair: decides whether long chunk tiles are split along the keys
+  int chunk_step_cost;
   PlanHeader* hdr;
   int32_t* tile_prefix;
   int32_t* dec_prefix;
@@ -67,25 +70,46 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int s_carry[3];
   __shared__ int s_pass_tot[3];
   __shared__ int s_bad;
+  __shared__ long long s_cstat[32][4];  // per group: chunk steps, decode keys, chunk tiles, max steps
+  __shared__ int s_csplit;
   const int tid = threadIdx.x;
   if (tid == 0) s_bad = 0;
 
-  // 1. decode work and partial-slot counts for every candidate split size.
+  // 1. decode work and partial-slot counts for every candidate split size; the
+  // candidate-0 lanes also total the work estimate used for chunk splits.  Tile
+  // t of a chunk with history H0 covers keys [0, min(Lk, H0 + 128 (t + 1))),
+  // so every tile but the last takes ceil(H0 / 64) + 2 (t + 1) steps of 64 keys.
   {
     const int k = tid & 31, grp = tid >> 5;
-    long long items = 0, parts = 0;
+    long long items = 0, parts = 0, csteps = 0, dkeys = 0, ctiles = 0, cmax = 0;
     if (k < kSplitCandidates) {
       const long long split = static_cast<long long>(kSplitMin) << k;
       for (int b = grp; b < a.num_seqs; b += 32) {
         int lq, lk;
-        if (!plan_segment(a, b, lq, lk) || lq != 1) continue;
-        const long long n = (lk + split - 1) / split;
-        items += n;
-        parts += n > 1 ? n : 0;
+        if (!plan_segment(a, b, lq, lk)) continue;
+        if (lq == 1) {
+          const long long n = (lk + split - 1) / split;
+          items += n;
+          parts += n > 1 ? n : 0;
+          dkeys += lk;
+        } else if (lq >= 2) {
+          const long long nt = (lq + kChunkRows - 1) / kChunkRows;
+          const long long h0_steps = (static_cast<long long>(lk - lq) + 63) / 64;
+          const long long last = (lk + 63) / 64;
+          csteps += (nt - 1) * h0_steps + (nt - 1) * nt + last;
+          ctiles += nt;
+          cmax = max(cmax, last);
+        }
       }
     }
     s_items[grp][k] = items;
     s_parts[grp][k] = parts;
+    if (k == 0) {
+      s_cstat[grp][0] = csteps;
+      s_cstat[grp][1] = dkeys;
+      s_cstat[grp][2] = ctiles;
+      s_cstat[grp][3] = cmax;
+    }
   }
   __syncthreads();
   if (tid < 32) {
@@ -96,6 +120,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     }
     s_items[0][tid] = items;
     s_parts[0][tid] = parts;
+  } else if (tid < 36) {
+    const int c = tid - 32;
+    long long v = 0;
+    for (int g = 0; g < 32; ++g) v = c == 3 ? max(v, s_cstat[g][c]) : v + s_cstat[g][c];
+    s_cstat[0][c] = v;
   }
   __syncthreads();
   if (tid == 0) {
@@ -111,9 +140,30 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     }
     s_split_log = pick;
     for (int c = 0; c < 3; ++c) s_carry[c] = 0;
+    // Chunk tiles are split along the keys when the longest one alone would
+    // outlast an even share of the whole step's work; then every chunk tile is
+    // cut into S ranges, within the item, slot and minimum-length limits.
+    int S = 1;
+    const long long n_ct = s_cstat[0][2], steps_max = s_cstat[0][3];
+    if (n_ct > 0 && n_ct <= a.tiles_cap) {
+      const double work = (static_cast<double>(s_cstat[0][0]) * a.chunk_step_cost +
+                           static_cast<double>(s_cstat[0][1])) * a.num_heads;
+      const double share = work / a.grid;
+      const double longest = static_cast<double>(steps_max) * a.chunk_step_cost;
+      if (longest > share) {
+        long long want = static_cast<long long>(ceil(longest / share));
+        want = min(want, static_cast<long long>(a.grid) / (n_ct * a.num_heads));
+        want = min(want, static_cast<long long>(kChunkSplitItems) / (n_ct * a.num_heads));
+        want = min(want, static_cast<long long>(a.chunk_slots_cap) / n_ct);
+        want = min(want, steps_max * 64 / kChunkSplitMinKeys);
+        S = static_cast<int>(max(want, 1LL));
+      }
+    }
+    s_csplit = S;
   }
   __syncthreads();
   const int split = kSplitMin << s_split_log;
+  const int csplit = s_csplit;
 
   // 2. exclusive prefix sums of chunk tiles, decode items and partial slots.
   const int lane = tid & (kWave - 1), wave = tid / kWave;
@@ -125,7 +175,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       if (!plan_segment(a, b, lq, lk)) {
         atomicAdd(&s_bad, 1);
       } else if (lq >= 2) {
-        v[0] = (lq + kChunkRows - 1) / kChunkRows;  // query tiles (per head)
+        v[0] = (lq + kChunkRows - 1) / kChunkRows * csplit;  // (query tile, split) pairs per head
       } else if (lq == 1) {
         const int n = (lk + split - 1) / split;
         v[1] = n * a.head_groups;
@@ -171,6 +221,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     a.hdr->n_dec_items = s_carry[1];
     a.hdr->n_parts = s_carry[2];
     a.hdr->split = split;
+    a.hdr->chunk_split = csplit;
     a.hdr->bad_segments = s_bad;
     // the attention kernel hands out the first item of every workgroup statically:
     // chunk-first workgroup b takes item b / 8 of chunk group b % 8, decode-first
@@ -201,6 +252,7 @@ struct MainArgs {
   const int32_t* dec_prefix;
   const int32_t* part_prefix;
   float* partials;
+  float* chunk_partials;  // [slot][head][128 rows][part_stride] of split chunk tiles
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -246,9 +298,52 @@ template <> struct ChunkCfg<float> {
   };
 };
 
-// ---------------------------------------------------------------- chunk role, bf16
+// ---------------------------------------------------------------- chunk KV splits
+// Keys [kb0, kb1) of split `split` out of `nsplit` of a chunk tile whose keys
+// are [0, kend): equal ranges rounded up to 64 keys, so every range boundary
+// other than kend falls on a 64-key step (keys past a range end are never
+// loaded and never need a mask).  Late ranges of short tiles may be empty.
+__device__ __forceinline__ void chunk_key_range(int kend, int split, int nsplit, int& kb0, int& kb1) {
+  if (nsplit == 1) {
+    kb0 = 0;
+    kb1 = kend;
+    return;
+  }
+  const int ck = ((kend + nsplit - 1) / nsplit + 63) & ~63;
+  kb0 = min(split * ck, kend);
+  kb1 = min(kb0 + ck, kend);
+}
+
+// A split chunk tile: each (tile, head, key range) item leaves fp32 rows
+// (m in log2 units, l, acc[D]) in its slot of chunk_partials; combine_kernel
+// merges the ranges of every row after the attention launch.
 template <int D>
-__device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, unsigned char* smem) {
+__device__ __forceinline__ void chunk_store_partial(const MainArgs& a, int seg, int h, int tile,
+                                                    int split, int nsplit, float m_log2, float l_tot,
+                                                    const f32x16_t (&acc)[D / 32]) {
+  constexpr int NM = D / 32;
+  const int lane = threadIdx.x & 63, w = wave_id(), qc = lane & 31, g = lane >> 5;
+  const int slot = a.tile_prefix[seg] + tile * nsplit + split;
+  float* pp = a.chunk_partials +
+              ((static_cast<size_t>(slot) * a.num_heads + h) * kChunkRows + w * 32 + qc) * a.part_stride;
+  if (g == 0) *reinterpret_cast<float2*>(pp) = float2{m_log2, l_tot};
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4)
+      *reinterpret_cast<f32x4_t*>(pp + 4 + m * 32 + i4 * 8 + g * 4) =
+          f32x4_t{acc[m][4 * i4], acc[m][4 * i4 + 1], acc[m][4 * i4 + 2], acc[m][4 * i4 + 3]};
+}
+
+// ---------------------------------------------------------------- chunk role, bf16
+// kSplit: the tile is one of nsplit key ranges (else nsplit == 1, split == 0)
+template <int D, bool kSplit>
+__device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, int split, int nsplit,
+                                unsigned char* smem) {
+  if constexpr (!kSplit) {
+    split = 0;
+    nsplit = 1;
+  }
   using Cfg = ChunkCfg<bf16_t>::Sizes<D>;
   constexpr int BN = Cfg::BN, NKB = BN / 32, KS = D / 16, NM = D / 32;
   constexpr int KROW = Cfg::KROW, VROW = Cfg::VROW, STAGE = Cfg::STAGE;
@@ -264,6 +359,8 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, uns
   const int row0 = tile * kChunkRows;
   const int rows_end = min(row0 + kChunkRows, Lq);
   const int kend = H0 + rows_end;  // keys [0, kend) are visible to some row of the tile
+  int kb0, kb1;                    // this item's keys
+  chunk_key_range(kend, split, nsplit, kb0, kb1);
   const int wrow0 = row0 + w * 32;
   const int my_row = wrow0 + qc;
   const bool wave_active = wrow0 < rows_end;
@@ -287,10 +384,10 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, uns
   // Tile loads.  Every 16-byte load of a tile reads from one page that is the
   // same for the whole wave (K load `it`: page (it*256 + 64w) / (16*CPR) of the
   // tile; V: page w), so page ids are scalar block-table reads and the gathers
-  // are buffer loads with a 32-bit lane offset.  Keys at or past kend read as
+  // are buffer loads with a 32-bit lane offset.  Keys at or past kb1 read as
   // zero (offset out of range, or an empty descriptor for whole pages).
   const_i32_t* btrow = (const_i32_t*)(a.bt) + static_cast<size_t>(seg) * a.max_blocks;
-  const int last_page = (kend - 1) >> 4;
+  const int last_page = (max(kb1, 1) - 1) >> 4;
   const uint32_t slot_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 2;
   const uint32_t page_bytes = slot_bytes * kPage;
   const uint32_t head_off = static_cast<uint32_t>(kvh) * D * 2;
@@ -317,7 +414,7 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, uns
 #pragma unroll
     for (int it = 0; it < KLOADS; ++it) {
       const int key = (it * kThreads + tid) / CPR;
-      const uint32_t off = (k0 + key < kend)
+      const uint32_t off = (k0 + key < kb1)
                                ? (key & 15) * slot_bytes + head_off + (tid % CPR) * 16
                                : kOffsetOutOfRange;
       const auto rs = rsrc(kpool, (it * kThreads + w * kWave) / (16 * CPR));
@@ -327,7 +424,7 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, uns
 #pragma unroll
     for (int t = 0; t < VKG; ++t) {
       const int key = vkg * VKG + t;
-      const uint32_t off = (k0 + key < kend)
+      const uint32_t off = (k0 + key < kb1)
                                ? (key & 15) * slot_bytes + head_off + vc_ * 16
                                : kOffsetOutOfRange;
       vreg[t] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
@@ -367,14 +464,16 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, uns
   // written into the other and tile i+2 streams into registers; one barrier
   // per tile.
   int ids_a[4], ids_b[4];
-  tile_ids(0, ids_a);
-  issue_tile(0, ids_a);
-  tile_ids(BN, ids_b);
-  store_tile(smem);
-  issue_tile(BN, ids_b);
-  tile_ids(2 * BN, ids_a);  // ids are read one tile ahead of their loads
-  __syncthreads();
-  for (int k0 = 0, i = 0; k0 < kend; k0 += BN, ++i) {
+  if (kb0 < kb1) {
+    tile_ids(kb0, ids_a);
+    issue_tile(kb0, ids_a);
+    tile_ids(kb0 + BN, ids_b);
+    store_tile(smem);
+    issue_tile(kb0 + BN, ids_b);
+    tile_ids(kb0 + 2 * BN, ids_a);  // ids are read one tile ahead of their loads
+    __syncthreads();
+  }
+  for (int k0 = kb0, i = 0; k0 < kb1; k0 += BN, ++i) {
     const unsigned char* Ks = smem + (i & 1) * STAGE;
     const unsigned char* Vt = Ks + BN * KROW;
     if (wave_active && k0 <= H0 + wrow0 + 31) {  // else the tile is invisible to this wave
@@ -457,7 +556,7 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, uns
         }
       }
     }
-    if (k0 + BN < kend) {
+    if (k0 + BN < kb1) {
       store_tile(smem + ((i + 1) & 1) * STAGE);  // tile i+1, loaded during tile i
       issue_tile(k0 + 2 * BN, ids_a);           // tile i+2 streams in
       tile_ids(k0 + 3 * BN, ids_a);
@@ -466,7 +565,12 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, uns
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);  // lanes l and l^32 share a row
-  if (!wave_active || my_row >= Lq) return;
+  const bool row_ok = wave_active && my_row < Lq;
+  if (!row_ok) return;
+  if constexpr (kSplit) {
+    chunk_store_partial<D>(a, seg, h, tile, split, nsplit, m_run * a.scale_log2, l_tot, acc);
+    return;
+  }
   const float inv = 1.f / l_tot;
   bf16_t* op = static_cast<bf16_t*>(a.out) + (static_cast<size_t>(q0 + my_row) * a.num_heads + h) * D;
 #pragma unroll
@@ -481,8 +585,13 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, uns
 }
 
 // ---------------------------------------------------------------- chunk role, fp32
-template <int D>
-__device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, unsigned char* smem) {
+template <int D, bool kSplit>
+__device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, int split, int nsplit,
+                               unsigned char* smem) {
+  if constexpr (!kSplit) {
+    split = 0;
+    nsplit = 1;
+  }
   using Cfg = ChunkCfg<float>::Sizes<D>;
   constexpr int BN = Cfg::BN, NKB = BN / 32, KS = D / 2, NM = D / 32, ROWF = Cfg::ROWF;
   constexpr int CPR = D / 4;
@@ -498,6 +607,8 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, unsi
   const int row0 = tile * kChunkRows;
   const int rows_end = min(row0 + kChunkRows, Lq);
   const int kend = H0 + rows_end;
+  int kb0, kb1;  // this item's keys
+  chunk_key_range(kend, split, nsplit, kb0, kb1);
   const int wrow0 = row0 + w * 32;
   const int my_row = wrow0 + qc;
   const bool wave_active = wrow0 < rows_end;
@@ -517,9 +628,9 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, unsi
   float m_run = -INFINITY, l_run = 0.f;
 
   // Tile loads as in the bf16 role: load `it` of every thread reads one page,
-  // uniform per wave, through a buffer descriptor; keys at or past kend read 0.
+  // uniform per wave, through a buffer descriptor; keys at or past kb1 read 0.
   const_i32_t* btrow = (const_i32_t*)(a.bt) + static_cast<size_t>(seg) * a.max_blocks;
-  const int last_page = (kend - 1) >> 4;
+  const int last_page = (max(kb1, 1) - 1) >> 4;
   const uint32_t slot_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 4;
   const uint32_t page_bytes = slot_bytes * kPage;
   const uint32_t head_off = static_cast<uint32_t>(kvh) * D * 4;
@@ -538,7 +649,7 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, unsi
     for (int it = 0; it < LOADS; ++it) {
       const int key = (it * kThreads + tid) / CPR;
       const int pidx = (it * kThreads + w * kWave) / (16 * CPR);  // uniform per wave
-      const uint32_t off = (k0 + key < kend)
+      const uint32_t off = (k0 + key < kb1)
                                ? (key & 15) * slot_bytes + head_off + (tid % CPR) * 16
                                : kOffsetOutOfRange;
       const auto kr = page_rsrc(kpool, k0, pidx);
@@ -548,8 +659,8 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, unsi
     }
   };
 
-  issue_tile(0);
-  for (int k0 = 0; k0 < kend; k0 += BN) {
+  if (kb0 < kb1) issue_tile(kb0);
+  for (int k0 = kb0; k0 < kb1; k0 += BN) {
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
@@ -616,7 +727,12 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, unsi
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);  // lanes l and l^32 share a row
-  if (!wave_active || my_row >= Lq) return;
+  const bool row_ok = wave_active && my_row < Lq;
+  if (!row_ok) return;
+  if constexpr (kSplit) {
+    chunk_store_partial<D>(a, seg, h, tile, split, nsplit, m_run, l_tot, acc);
+    return;
+  }
   const float inv = 1.f / l_tot;
   float* op = static_cast<float*>(a.out) + (static_cast<size_t>(q0 + my_row) * a.num_heads + h) * D;
 #pragma unroll
@@ -1021,12 +1137,14 @@ __device__ __forceinline__ int find_segment_lds(const int* prefix, int n, int x)
   return lo;
 }
 
-template <typename T, int D>
+// kSplit: this launch may meet split chunk tiles (the planner was allowed to
+// split); the instance without it keeps the unsplit roles' register allocation.
+template <typename T, int D, bool kSplit>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
   constexpr int kSmem = ChunkCfg<T>::template Sizes<D>::BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kSmem];
   __shared__ int s_prefix[2][kLdsSegments + 1];
-  __shared__ int s_work[4];
+  __shared__ int s_work[5];
   // scheduler state, touched by thread 0 only; kept in LDS so no register holds
   // it across work items
   __shared__ int s_next;           // item claimed for the next iteration
@@ -1035,6 +1153,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
   const int n_tiles = a.hdr->n_chunk_tiles;
   const int n_dec = a.hdr->n_dec_items;
   const int split_keys = a.hdr->split;
+  const int csplit = kSplit ? a.hdr->chunk_split : 1;
   const bool lds_lookup = a.num_seqs <= kLdsSegments;
   if (lds_lookup) {
     for (int i = threadIdx.x; i <= a.num_seqs; i += kThreads) {
@@ -1109,7 +1228,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
   for (;;) {
     if (threadIdx.x == 0) {
       const int cur = s_next;
-      int kind = 0, seg = 0, p1 = 0, p2 = 0;  // kind: 0 done, 1 chunk, 2 decode
+      int kind = 0, seg = 0, p1 = 0, p2 = 0, p3 = 0;  // kind: 0 done, 1 chunk, 2 decode
       if (cur != kDone && (cur & kDecodeTag)) {
         const int d = cur & (kDecodeTag - 1);
         seg = lds_lookup ? find_segment_lds(s_prefix[1], a.num_seqs, d)
@@ -1117,23 +1236,30 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
         p1 = d - (lds_lookup ? s_prefix[1][seg] : a.dec_prefix[seg]);
         kind = 2;
       } else if (cur != kDone) {
-        // group x holds, segment by segment, (head x + 8k, tile) for its heads
+        // group x holds, segment by segment, (head x + 8k, tile, split) for its
+        // heads; tile_prefix counts (tile, split) pairs
         const int x = cur >> 24, i = cur & ((1 << 24) - 1);
         const int nh = chunk_group_heads(a.num_heads, x);
-        const int t = i / nh;  // tile rank over all segments, scaled down by the group's heads
+        const int t = i / nh;  // pair rank over all segments, scaled down by the group's heads
         seg = lds_lookup ? find_segment_lds(s_prefix[0], a.num_seqs, t)
                          : find_segment(a.tile_prefix, a.num_seqs, t);
         const int t0 = lds_lookup ? s_prefix[0][seg] : a.tile_prefix[seg];
-        const int nt = (lds_lookup ? s_prefix[0][seg + 1] : a.tile_prefix[seg + 1]) - t0;
-        const int local = i - nh * t0;
-        p1 = x + kXcdGroups * (local / nt);   // query head
-        p2 = nt - 1 - local % nt;             // query tile, longest first
+        const int nts = (lds_lookup ? s_prefix[0][seg + 1] : a.tile_prefix[seg + 1]) - t0;
+        const int local = i - nh * t0, r = local % nts;
+        p1 = x + kXcdGroups * (local / nts);  // query head
+        if (csplit == 1) {
+          p2 = nts - 1 - r;                   // query tile, longest first
+        } else {
+          p2 = nts / csplit - 1 - r / csplit;
+          p3 = r % csplit;                    // key range of the tile
+        }
         kind = 1;
       }
       s_work[0] = kind;
       s_work[1] = seg;
       s_work[2] = p1;
       s_work[3] = p2;
+      s_work[4] = p3;
     }
     __syncthreads();
     // the work item is uniform across the workgroup: keep it in scalar registers so
@@ -1142,12 +1268,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
     const int seg = __builtin_amdgcn_readfirstlane(s_work[1]);
     const int p1 = __builtin_amdgcn_readfirstlane(s_work[2]);
     const int p2 = __builtin_amdgcn_readfirstlane(s_work[3]);
+    const int p3 = __builtin_amdgcn_readfirstlane(s_work[4]);
     __syncthreads();
     if (kind == 0) break;
     if (threadIdx.x == 0) s_next = claim();  // next item, claimed while this one runs
     if (kind == 1) {
-      if constexpr (sizeof(T) == 2) chunk_tile_bf16<D>(a, seg, p1, p2, smem);
-      else chunk_tile_f32<D>(a, seg, p1, p2, smem);
+      if (csplit == 1) {
+        if constexpr (sizeof(T) == 2) chunk_tile_bf16<D, false>(a, seg, p1, p2, 0, 1, smem);
+        else chunk_tile_f32<D, false>(a, seg, p1, p2, 0, 1, smem);
+      } else if constexpr (kSplit) {
+        if constexpr (sizeof(T) == 2) chunk_tile_bf16<D, true>(a, seg, p1, p2, p3, csplit, smem);
+        else chunk_tile_f32<D, true>(a, seg, p1, p2, p3, csplit, smem);
+      }
     } else {
       if constexpr (sizeof(T) == 2) decode_item_bf16<D>(a, seg, p1, split_keys);
       else decode_item<T, D>(a, seg, p1, split_keys);
@@ -1156,12 +1288,67 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
 }
 
 // ---------------------------------------------------------------- combine
+// Workgroups past the decode ones merge split chunk tiles: each takes
+// (tile, head) pairs in turn; 4 threads per query row, D / 4 channels each.
+constexpr int kChunkMergeBlocks = 64;
+
+template <typename T, int D>
+__device__ void merge_chunk_tiles(const MainArgs& a, int blk) {
+  const int S = a.hdr->chunk_split;
+  if (S <= 1) return;
+  constexpr int QPR = 4, CPT = D / QPR, NV = CPT / 4;
+  const int n_pairs = a.hdr->n_chunk_tiles / S * a.num_heads;
+  const size_t sstep = static_cast<size_t>(a.num_heads) * kChunkRows * a.part_stride;
+  const int c0 = (threadIdx.x % QPR) * CPT;
+  for (int p = blk; p < n_pairs; p += kChunkMergeBlocks) {
+    const int ti = p / a.num_heads, h = p - ti * a.num_heads;  // tile over all chunk segments
+    const int seg = find_segment(a.tile_prefix, a.num_seqs, ti * S);
+    const int tile = ti - a.tile_prefix[seg] / S;
+    const int q0 = a.cu[seg], Lq = a.cu[seg + 1] - q0;
+    const size_t slot0 = static_cast<size_t>(a.tile_prefix[seg] + tile * S);
+    for (int rr = threadIdx.x / QPR; rr < kChunkRows; rr += kThreads / QPR) {
+      const int row = tile * kChunkRows + rr;
+      if (row >= Lq) break;
+      const float* base = a.chunk_partials + ((slot0 * a.num_heads + h) * kChunkRows + rr) * a.part_stride;
+      float mx = -INFINITY;  // finite: range 0 holds key 0, which every row sees
+      for (int sp = 0; sp < S; ++sp) mx = fmaxf(mx, base[sp * sstep]);
+      float l = 0.f;
+      f32x4_t o[NV];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int sp = 0; sp < S; ++sp) {
+        const float* pp = base + sp * sstep;
+        const float wgt = fast_exp2(pp[0] - mx);
+        l = fmaf(pp[1], wgt, l);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) o[i] += wgt * *reinterpret_cast<const f32x4_t*>(pp + 4 + c0 + 4 * i);
+      }
+      const float inv = 1.f / l;
+      T* op = static_cast<T*>(a.out) + (static_cast<size_t>(q0 + row) * a.num_heads + h) * D + c0;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const f32x4_t v = o[i] * inv;
+        if constexpr (sizeof(T) == 2) {
+          st8(op + 4 * i, u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
+        } else {
+          *reinterpret_cast<f32x4_t*>(op + 4 * i) = v;
+        }
+      }
+    }
+  }
+}
+
 // One wave per (decode segment, head) that was split: lanes first reduce the
 // split maxima, then every lane owns D / 64 channels and sums the rescaled
 // partial accumulators of all splits.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void combine_kernel(MainArgs a) {
   const int head_groups = (a.num_heads + kHeadsPerDecodeItem - 1) / kHeadsPerDecodeItem;
+  const int n_dec_blocks = a.num_seqs * head_groups;
+  if (static_cast<int>(blockIdx.x) >= n_dec_blocks) {
+    merge_chunk_tiles<T, D>(a, blockIdx.x - n_dec_blocks);
+    return;
+  }
   const int seg = blockIdx.x / head_groups, hg = blockIdx.x - seg * head_groups;
   const int p0 = a.part_prefix[seg], np = a.part_prefix[seg + 1] - p0;
   if (np <= 0) return;
@@ -1222,20 +1409,36 @@ namespace {
 
 struct DeviceInfo {
   int cus = 0;
-  int slots[2][2] = {{0, 0}, {0, 0}};  // [dtype][D == 128] resident workgroups per CU
+  int slots[2][2][2] = {};  // [dtype][D == 128][split-capable] resident workgroups per CU
 };
 
 DeviceInfo g_info[64];
 
+hipError_t occupancy(DeviceInfo& info, int dt, int di, int ds, const void* kernel, int& grid) {
+  if (info.slots[dt][di][ds] == 0) {
+    int n = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kThreads, 0);
+    if (e != hipSuccess) return e;
+    info.slots[dt][di][ds] = n > 0 ? n : 1;
+  }
+  grid = info.cus * info.slots[dt][di][ds];
+  return hipSuccess;
+}
+
 template <typename T, int D>
 hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dt, int di) {
-  if (info.slots[dt][di] == 0) {
-    int n = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_kernel<T, D>, kThreads, 0);
+  // Chunk tiles may be split only when even the largest number of them the
+  // bounds allow (tiles_cap per head) fills at most half of the resident
+  // workgroups; every other step runs the instance without the split code.
+  int grid = 0;
+  hipError_t e = occupancy(info, dt, di, 0, reinterpret_cast<const void*>(attn_kernel<T, D, false>), grid);
+  if (e != hipSuccess) return e;
+  const bool split_ok = L.ws.chunk_slots_cap >= 2 &&
+                        2LL * L.ws.tiles_cap * L.num_heads <= static_cast<long long>(grid);
+  if (split_ok) {
+    e = occupancy(info, dt, di, 1, reinterpret_cast<const void*>(attn_kernel<T, D, true>), grid);
     if (e != hipSuccess) return e;
-    info.slots[dt][di] = n > 0 ? n : 1;
   }
-  const int grid = info.cus * info.slots[dt][di];
   unsigned char* ws = L.workspace;
   PlanHeader* hdr = reinterpret_cast<PlanHeader*>(ws);
   int32_t* tile_prefix = reinterpret_cast<int32_t*>(ws + L.ws.tile_prefix);
@@ -1243,19 +1446,27 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dt, int di) {
   int32_t* part_prefix = reinterpret_cast<int32_t*>(ws + L.ws.part_prefix);
   const int head_groups = (L.num_heads + kHeadsPerDecodeItem - 1) / kHeadsPerDecodeItem;
 
+  // cost of a 64-key chunk step in decode (key, head) pairs, measured roughly on
+  // MI355X: a bf16 step at D = 128 takes about as long as streaming 128 decode
+  // keys of one head; fp32 and D = 64 steps cost relatively more
+  const int chunk_step_cost = (sizeof(T) == 4 || D == 64) ? 192 : 128;
   PlanArgs pa{L.cu_seqlens_q, L.seqlens_k, L.num_seqs, L.total_q, L.max_seqlen_q, L.max_seqlen_k,
               L.max_blocks, L.num_heads, head_groups, L.ws.parts_cap, grid * kItemsPerSlot,
-              grid, hdr, tile_prefix, dec_prefix, part_prefix};
+              grid, L.ws.tiles_cap, split_ok ? L.ws.chunk_slots_cap : 0, chunk_step_cost, hdr,
+              tile_prefix, dec_prefix, part_prefix};
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, L.stream, pa);
 
   MainArgs ma{L.q, L.k_cache, L.v_cache, L.out, L.cu_seqlens_q, L.seqlens_k, L.block_table,
               L.num_seqs, L.num_heads, L.num_kv_heads, L.num_heads / L.num_kv_heads,
               L.num_blocks, L.max_blocks, L.ws.part_stride, L.sm_scale * kLog2e, hdr,
               tile_prefix, dec_prefix, part_prefix,
-              reinterpret_cast<float*>(ws + L.ws.partials)};
-  hipLaunchKernelGGL((attn_kernel<T, D>), dim3(grid), dim3(kThreads), 0, L.stream, ma);
-  hipLaunchKernelGGL((combine_kernel<T, D>), dim3(L.num_seqs * head_groups), dim3(kThreads), 0,
-                     L.stream, ma);
+              reinterpret_cast<float*>(ws + L.ws.partials),
+              reinterpret_cast<float*>(ws + L.ws.chunk_partials)};
+  if (split_ok) hipLaunchKernelGGL((attn_kernel<T, D, true>), dim3(grid), dim3(kThreads), 0, L.stream, ma);
+  else hipLaunchKernelGGL((attn_kernel<T, D, false>), dim3(grid), dim3(kThreads), 0, L.stream, ma);
+  const int merge_blocks = split_ok ? kChunkMergeBlocks : 0;
+  hipLaunchKernelGGL((combine_kernel<T, D>), dim3(L.num_seqs * head_groups + merge_blocks),
+                     dim3(kThreads), 0, L.stream, ma);
   return hipGetLastError();
 }
 

@@ -18,10 +18,17 @@ constexpr int kPartsMax = 16384;    // cap on (segment, split) partial slots
 constexpr int kItemsPerSlot = 16;   // decode work items aimed at per resident workgroup
 constexpr int kHeadsPerDecodeItem = 4;  // one head per wave
 constexpr int kMaxSeqlenK = 1 << 30;
+// Chunk tiles are split along the keys only when a few long tiles would
+// otherwise outlast the rest of the step: at most this many (tile, head, split)
+// items in all, each split at least kChunkSplitMinKeys keys long.
+constexpr int kChunkSplitItems = 512;
+constexpr int kChunkSplitMinKeys = 512;
 
 // ---- workspace ---------------------------------------------------------------------
 // [header 256 B][tile_prefix (B+1)][dec_prefix (B+1)][part_prefix (B+1)]
-// [partials parts_cap x H x (D + 4) fp32]; every array starts on a 256-byte boundary.
+// [partials parts_cap x H x (D + 4) fp32]
+// [chunk_partials chunk_slots_cap x H x 128 x (D + 4) fp32]; every array starts
+// on a 256-byte boundary.
 // Chunk tiles are queued in kXcdGroups groups: the tiles of query head h go to
 // group h % kXcdGroups, and workgroup b prefers group b % kXcdGroups.  Work-
 // groups are dispatched to the 8 XCDs of an MI355X round robin, so the query
@@ -40,16 +47,19 @@ struct PlanHeader {
   int32_t split;          // decode split size in keys (multiple of 64)
   int32_t n_parts;        // partial slots in use
   int32_t bad_segments;   // segments skipped because they broke a precondition
-  int32_t pad[50];
+  int32_t chunk_split;    // KV splits per chunk tile (1: tiles are not split)
+  int32_t pad[49];
 };
 static_assert(sizeof(PlanHeader) == 256, "header is 256 bytes");
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t tile_prefix, dec_prefix, part_prefix, partials, total;
+  size_t tile_prefix, dec_prefix, part_prefix, partials, chunk_partials, total;
   int parts_cap;
-  int part_stride;  // floats per (part, head): m, l, 2 pad, acc[D]
+  int part_stride;      // floats per (part, head) or (chunk slot, head, row): m, l, 2 pad, acc[D]
+  int tiles_cap;        // bound on query tiles over all chunk segments
+  int chunk_slots_cap;  // (tile, split) partial slots available to split chunk tiles
 };
 
 inline int parts_cap_for(int num_seqs, int max_seqlen_k) {
@@ -58,7 +68,23 @@ inline int parts_cap_for(int num_seqs, int max_seqlen_k) {
   return static_cast<int>(cap < kPartsMax ? cap : kPartsMax);
 }
 
-inline WsLayout ws_layout(int num_seqs, int max_seqlen_k, int num_heads, int head_dim) {
+// Query tiles of all chunk segments: a chunk segment has Lq >= 2 rows, so there
+// are at most total_q / 2 of them and sum(ceil(Lq / 128)) <= total_q / 128 + #chunks.
+inline int tiles_cap_for(int num_seqs, int total_q) {
+  const long long chunks = num_seqs < total_q / 2 ? num_seqs : total_q / 2;
+  return static_cast<int>(total_q / kChunkRows + chunks);
+}
+
+inline int chunk_slots_cap_for(int num_seqs, int total_q, int max_seqlen_k, int num_heads) {
+  const long long by_items = kChunkSplitItems / num_heads;
+  const long long max_split = (static_cast<long long>(max_seqlen_k) + kChunkSplitMinKeys - 1) /
+                              kChunkSplitMinKeys;
+  const long long by_shape = static_cast<long long>(tiles_cap_for(num_seqs, total_q)) * max_split;
+  const long long cap = by_items < by_shape ? by_items : by_shape;
+  return static_cast<int>(cap < 2 ? 0 : cap);
+}
+
+inline WsLayout ws_layout(int num_seqs, int total_q, int max_seqlen_k, int num_heads, int head_dim) {
   WsLayout l;
   size_t off = sizeof(PlanHeader);
   size_t arr = align256(sizeof(int32_t) * (static_cast<size_t>(num_seqs) + 1));
@@ -69,6 +95,11 @@ inline WsLayout ws_layout(int num_seqs, int max_seqlen_k, int num_heads, int hea
   l.part_stride = head_dim + 4;
   l.partials = off;
   off += align256(sizeof(float) * static_cast<size_t>(l.parts_cap) * num_heads * l.part_stride);
+  l.tiles_cap = tiles_cap_for(num_seqs, total_q);
+  l.chunk_slots_cap = chunk_slots_cap_for(num_seqs, total_q, max_seqlen_k, num_heads);
+  l.chunk_partials = off;
+  off += align256(sizeof(float) * static_cast<size_t>(l.chunk_slots_cap) * num_heads * kChunkRows *
+                  l.part_stride);
   l.total = off;
   return l;
 }

@@ -90,8 +90,10 @@ ha_status paged_kv_append(const void* key, const void* value, const int32_t* slo
 
 /*
  * hybrid_attn_workspace_size -- bytes of device workspace hybrid_attn_fwd
- * needs for a step with these bounds (plan arrays, work counter and split-KV
- * partial results).  Depends only on host-known bounds.
+ * needs for a step with these bounds (plan arrays, work counters, split-KV
+ * partial results of decode rows and of long chunk tiles).  Depends only on
+ * host-known bounds; returns 0
+ * for num_seqs < 1, total_q < 0, max_seqlen_k < 0, num_heads < 1 or head_dim < 1.
  */
 size_t hybrid_attn_workspace_size(int32_t num_seqs, int32_t total_q, int32_t max_seqlen_k,
                                   int32_t num_heads, int32_t head_dim);

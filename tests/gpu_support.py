@@ -44,6 +44,17 @@ def gpu_step(ds: W.DeviceStep, workspace=None, append=True):
     return out
 
 
+PLAN_HEADER_FIELDS = ("dec_counter", "n_chunk_tiles", "n_dec_items", "split", "n_parts",
+                      "bad_segments", "chunk_split")
+
+
+def plan_header(workspace) -> dict:
+    """The planner's summary of the last call, read from the workspace head
+    (8 chunk-group counters, then the int32 fields above, in order)."""
+    raw = workspace[:64].cpu().numpy().view(np.int32)
+    return dict(zip(PLAN_HEADER_FIELDS, (int(v) for v in raw[8:8 + len(PLAN_HEADER_FIELDS)])))
+
+
 def to_f64(t) -> np.ndarray:
     return O.to_f64(W.to_host_array(t))
 

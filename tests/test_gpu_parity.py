@@ -68,6 +68,40 @@ def _dev(hs):
     return W.to_device(hs, "cuda")
 
 
+# ---------------------------------------------------------------- chunk KV splits
+# Few, long chunk tiles and little decode work: the planner cuts every chunk
+# tile into key ranges whose partial results the last range to finish merges.
+SPLIT_CASES = [
+    # (segments (Lq, Lk), Hq, Hkv, D, dtype, seed)
+    ([(200, 1000)], 2, 2, 128, W.BF16, 21),
+    ([(1000, 1000)], 1, 1, 64, W.BF16, 22),              # no history: empty late ranges
+    ([(130, 8000)], 1, 1, 64, W.BF16, 23),               # many ranges, ragged last tile
+    ([(300, 3000), (1, 100)], 2, 2, 128, W.F32, 24),
+    ([(1, 700), (257, 2900), (1, 33)], 4, 2, 64, W.F32, 25),   # GQA
+    ([(77, 5000), (1, 5), (400, 1400)], 2, 2, 128, W.BF16, 26),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SPLIT_CASES)))
+def test_chunk_split(case):
+    segs, hq, hkv, d, dt, seed = SPLIT_CASES[case]
+    spec, meta = W.custom_step(segs, hq, hkv, d, dt, seed=seed)
+    hs = W.host_values(spec, meta, seed=seed)
+    ds = _dev(hs)
+    ref, kc_ref, vc_ref = G.oracle_full(ds, hs.k_cache, hs.v_cache)
+    G.note(f"chunk_split case={case} segs={segs} H={hq}/{hkv} D={d} {dt}")
+    ws = B.alloc_workspace(meta.num_seqs, meta.total_q, meta.max_seqlen_k, hq, d)
+    out = G.gpu_step(ds, workspace=ws)
+    hdr = G.plan_header(ws)
+    assert hdr["chunk_split"] > 1, hdr
+    kc, vc = G.host_pools(ds)
+    assert kc.tobytes() == kc_ref.tobytes() and vc.tobytes() == vc_ref.tobytes()
+    G.compare(G.to_f64(out), ref, dt, f"split case {case}")
+    # a second call on the same workspace (counters left over from the first)
+    out2 = G.gpu_step(ds, workspace=ws, append=False)
+    G.compare(G.to_f64(out2), ref, dt, f"split case {case}, second call")
+
+
 # ---------------------------------------------------------------- full configs
 def test_config1_worked_example():
     spec, meta = W.make_step(1)
@@ -75,7 +109,10 @@ def test_config1_worked_example():
     ds = _dev(hs)
     ref, kc_ref, vc_ref = G.oracle_full(ds, hs.k_cache, hs.v_cache)
     G.note("config1 worked example fp32 H=2 D=64")
-    out = G.gpu_step(ds)
+    ws = B.alloc_workspace(meta.num_seqs, meta.total_q, meta.max_seqlen_k, spec.num_heads,
+                           spec.head_dim)
+    out = G.gpu_step(ds, workspace=ws)
+    assert G.plan_header(ws)["chunk_split"] > 1  # 30 long tiles on a whole GPU: split
     kc, vc = G.host_pools(ds)
     assert kc.tobytes() == kc_ref.tobytes() and vc.tobytes() == vc_ref.tobytes()
     G.compare(G.to_f64(out), ref, W.F32, "config 1")
