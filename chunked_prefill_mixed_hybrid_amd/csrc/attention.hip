@@ -63,39 +63,59 @@ __device__ __forceinline__ bool plan_segment(const PlanArgs& a, int b, int& lq, 
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
+  __shared__ int s_lq[kPlanThreads], s_lk[kPlanThreads];  // shapes of the first segments; lq -1: skipped
   __shared__ long long s_items[32][32];
   __shared__ long long s_parts[32][32];
-  __shared__ int s_split_log;
+  __shared__ long long s_cstat[32][4];  // per group: chunk steps, decode keys, chunk tiles, max steps
+  __shared__ int s_split_log, s_csplit;
   __shared__ int s_wave_tot[kPlanThreads / kWave][3];
   __shared__ int s_carry[3];
   __shared__ int s_pass_tot[3];
   __shared__ int s_bad;
-  __shared__ long long s_cstat[32][4];  // per group: chunk steps, decode keys, chunk tiles, max steps
-  __shared__ int s_csplit;
   const int tid = threadIdx.x;
-  if (tid == 0) s_bad = 0;
+  const bool cached = a.num_seqs <= kPlanThreads;
 
-  // 1. decode work and partial-slot counts for every candidate split size; the
-  // candidate-0 lanes also total the work estimate used for chunk splits.  Tile
-  // t of a chunk with history H0 covers keys [0, min(Lk, H0 + 128 (t + 1))),
-  // so every tile but the last takes ceil(H0 / 64) + 2 (t + 1) steps of 64 keys.
+  // 0. every thread reads the shape of segment tid once
+  int my_lq = -1, my_lk = 0;
+  if (tid < a.num_seqs) {
+    int lq, lk;
+    if (plan_segment(a, tid, lq, lk)) {
+      my_lq = lq;
+      my_lk = lk;
+    }
+  }
+  s_lq[tid] = my_lq;
+  s_lk[tid] = my_lk;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+
+  // 1. decode work and partial-slot counts for every candidate split size
+  // (power-of-two sizes, so the divisions are shifts); the candidate-0 lanes
+  // also total the work estimate used for chunk splits.  Tile t of a chunk
+  // with history H0 covers keys [0, min(Lk, H0 + 128 (t + 1))), so every tile
+  // but the last takes ceil(H0 / 64) + 2 (t + 1) steps of 64 keys.
   {
     const int k = tid & 31, grp = tid >> 5;
     long long items = 0, parts = 0, csteps = 0, dkeys = 0, ctiles = 0, cmax = 0;
     if (k < kSplitCandidates) {
-      const long long split = static_cast<long long>(kSplitMin) << k;
+      const int sh = kSplitMinLog2 + k;
       for (int b = grp; b < a.num_seqs; b += 32) {
         int lq, lk;
-        if (!plan_segment(a, b, lq, lk)) continue;
+        if (cached) {
+          lq = s_lq[b];
+          lk = s_lk[b];
+        } else if (!plan_segment(a, b, lq, lk)) {
+          lq = -1;
+        }
         if (lq == 1) {
-          const long long n = (lk + split - 1) / split;
+          const long long n = (static_cast<long long>(lk) + (1LL << sh) - 1) >> sh;
           items += n;
           parts += n > 1 ? n : 0;
           dkeys += lk;
         } else if (lq >= 2) {
           const long long nt = (lq + kChunkRows - 1) / kChunkRows;
-          const long long h0_steps = (static_cast<long long>(lk - lq) + 63) / 64;
-          const long long last = (lk + 63) / 64;
+          const long long h0_steps = (static_cast<long long>(lk - lq) + 63) >> 6;
+          const long long last = (static_cast<long long>(lk) + 63) >> 6;
           csteps += (nt - 1) * h0_steps + (nt - 1) * nt + last;
           ctiles += nt;
           cmax = max(cmax, last);
@@ -112,57 +132,53 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     }
   }
   __syncthreads();
-  if (tid < 32) {
-    long long items = 0, parts = 0;
-    for (int g = 0; g < 32; ++g) {
-      items += s_items[g][tid];
-      parts += s_parts[g][tid];
+  // Wave 0 totals the groups: lanes 0..31 one candidate each, lanes 32..35 the
+  // chunk statistics; the split is the smallest candidate that fits the
+  // partial slots and keeps the decode item count near the target (the largest
+  // candidate, 2^30 keys, always fits).
+  if (tid < kWave) {
+    long long items = 0, parts = 0, stat = 0;
+    if (tid < 32) {
+      for (int g = 0; g < 32; ++g) {
+        items += s_items[g][tid];
+        parts += s_parts[g][tid];
+      }
+    } else if (tid < 36) {
+      const int c = tid - 32;
+      for (int g = 0; g < 32; ++g) stat = c == 3 ? max(stat, s_cstat[g][c]) : stat + s_cstat[g][c];
     }
-    s_items[0][tid] = items;
-    s_parts[0][tid] = parts;
-  } else if (tid < 36) {
-    const int c = tid - 32;
-    long long v = 0;
-    for (int g = 0; g < 32; ++g) v = c == 3 ? max(v, s_cstat[g][c]) : v + s_cstat[g][c];
-    s_cstat[0][c] = v;
+    const bool fits = tid < kSplitCandidates && parts <= a.parts_cap &&
+                      items * a.head_groups <= static_cast<long long>(a.target_items);
+    const unsigned long long fit_mask = __ballot(fits);
+    const long long csteps = __shfl(stat, 32), dkeys = __shfl(stat, 33);
+    const long long n_ct = __shfl(stat, 34), steps_max = __shfl(stat, 35);
+    if (tid == 0) {
+      s_split_log = fit_mask ? __ffsll(static_cast<long long>(fit_mask)) - 1 : kSplitCandidates - 1;
+      for (int c = 0; c < 3; ++c) s_carry[c] = 0;
+      // Chunk tiles are split along the keys when the longest one alone would
+      // outlast an even share of the whole step's work; then every chunk tile
+      // is cut into S ranges, within the item, slot and minimum-length limits.
+      int S = 1;
+      if (n_ct > 0 && n_ct <= a.tiles_cap && a.chunk_slots_cap >= 2) {
+        const double work = (static_cast<double>(csteps) * a.chunk_step_cost +
+                             static_cast<double>(dkeys)) * a.num_heads;
+        const double share = work / a.grid;
+        const double longest = static_cast<double>(steps_max) * a.chunk_step_cost;
+        if (longest > share) {
+          long long want = static_cast<long long>(ceil(longest / share));
+          want = min(want, static_cast<long long>(a.grid) / (n_ct * a.num_heads));
+          want = min(want, static_cast<long long>(kChunkSplitItems) / (n_ct * a.num_heads));
+          want = min(want, static_cast<long long>(a.chunk_slots_cap) / n_ct);
+          want = min(want, steps_max * 64 / kChunkSplitMinKeys);
+          S = static_cast<int>(max(want, 1LL));
+        }
+      }
+      s_csplit = S;
+    }
   }
   __syncthreads();
-  if (tid == 0) {
-    // smallest split that fits the partial slots and keeps the decode item
-    // count near the target; the largest candidate (2^30 keys) always fits.
-    int pick = kSplitCandidates - 1;
-    for (int k = 0; k < kSplitCandidates; ++k) {
-      if (s_parts[0][k] <= a.parts_cap &&
-          s_items[0][k] * a.head_groups <= static_cast<long long>(a.target_items)) {
-        pick = k;
-        break;
-      }
-    }
-    s_split_log = pick;
-    for (int c = 0; c < 3; ++c) s_carry[c] = 0;
-    // Chunk tiles are split along the keys when the longest one alone would
-    // outlast an even share of the whole step's work; then every chunk tile is
-    // cut into S ranges, within the item, slot and minimum-length limits.
-    int S = 1;
-    const long long n_ct = s_cstat[0][2], steps_max = s_cstat[0][3];
-    if (n_ct > 0 && n_ct <= a.tiles_cap) {
-      const double work = (static_cast<double>(s_cstat[0][0]) * a.chunk_step_cost +
-                           static_cast<double>(s_cstat[0][1])) * a.num_heads;
-      const double share = work / a.grid;
-      const double longest = static_cast<double>(steps_max) * a.chunk_step_cost;
-      if (longest > share) {
-        long long want = static_cast<long long>(ceil(longest / share));
-        want = min(want, static_cast<long long>(a.grid) / (n_ct * a.num_heads));
-        want = min(want, static_cast<long long>(kChunkSplitItems) / (n_ct * a.num_heads));
-        want = min(want, static_cast<long long>(a.chunk_slots_cap) / n_ct);
-        want = min(want, steps_max * 64 / kChunkSplitMinKeys);
-        S = static_cast<int>(max(want, 1LL));
-      }
-    }
-    s_csplit = S;
-  }
-  __syncthreads();
-  const int split = kSplitMin << s_split_log;
+  const int split_log = kSplitMinLog2 + s_split_log;
+  const int split = 1 << split_log;
   const int csplit = s_csplit;
 
   // 2. exclusive prefix sums of chunk tiles, decode items and partial slots.
@@ -171,13 +187,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     const int b = base + tid;
     int v[3] = {0, 0, 0};
     if (b < a.num_seqs) {
-      int lq, lk;
-      if (!plan_segment(a, b, lq, lk)) {
+      int lq = my_lq, lk = my_lk;
+      if (base > 0 && !plan_segment(a, b, lq, lk)) lq = -1;
+      if (lq < 0) {
         atomicAdd(&s_bad, 1);
       } else if (lq >= 2) {
         v[0] = (lq + kChunkRows - 1) / kChunkRows * csplit;  // (query tile, split) pairs per head
       } else if (lq == 1) {
-        const int n = (lk + split - 1) / split;
+        const int n = static_cast<int>((static_cast<unsigned>(lk) + split - 1u) >> split_log);
         v[1] = n * a.head_groups;
         v[2] = n > 1 ? n : 0;
       }
@@ -747,6 +764,10 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, int 
   }
 }
 
+// Work item codes of the persistent kernel: chunk item i of group x is
+// x << 24 | i, decode item d is kDecodeTag | d.
+constexpr int kDecodeTag = 1 << 28, kDone = 0x7fffffff;
+
 // ---------------------------------------------------------------- decode role
 // One wave = one head of one (segment, KV split).  Lane l = 16 r + c covers
 // channels [c * EPL, (c + 1) * EPL) of key rows 4u + r of each 64-key step.
@@ -1169,8 +1190,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
   // CU.  The first item of every workgroup is assigned statically (the planner
   // starts the counters past those items); afterwards the next item is claimed
   // with an atomic at the start of the current one, hiding the claim's latency.
-  // Item codes: chunk (group x, index i) = x << 24 | i; decode d = kDecodeTag | d.
-  constexpr int kDecodeTag = 1 << 28, kDone = 0x7fffffff;
   const int half = (gridDim.x + 1) / 2;
   const bool chunk_first = blockIdx.x < half;
   const int my_group = blockIdx.x % kXcdGroups;

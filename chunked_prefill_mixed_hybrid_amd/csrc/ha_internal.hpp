@@ -12,7 +12,8 @@ namespace ha {
 // ---- tuning constants (gfx950) ---------------------------------------------------
 constexpr int kThreads = 256;       // 4 waves per workgroup for every kernel role
 constexpr int kChunkRows = 128;     // query rows per chunk tile (32 per wave)
-constexpr int kSplitMin = 256;      // smallest decode KV split, in keys
+constexpr int kSplitMinLog2 = 8;
+constexpr int kSplitMin = 1 << kSplitMinLog2;  // smallest decode KV split, in keys
 constexpr int kSplitCandidates = 23;  // decode split sizes kSplitMin << k, k < 23 (up to 2^30)
 constexpr int kPartsMax = 16384;    // cap on (segment, split) partial slots
 constexpr int kItemsPerSlot = 16;   // decode work items aimed at per resident workgroup
