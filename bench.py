@@ -100,6 +100,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra steps each preceded by a 1 GiB cache-flush write")
+    ap.add_argument("--launch", default="fused", choices=["fused", "serial", "two-streams"],
+                    help="fused: hybrid_attn_fwd; serial / two-streams: the two-launch baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -122,11 +124,20 @@ def main():
     stream = torch.cuda.Stream()
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
 
+    def attention():
+        if args.launch == "fused":
+            B.hybrid_attn_fwd(ds.q, ds.k_cache, ds.v_cache, ds.cu_seqlens_q, ds.seqlens_k,
+                              ds.block_table, meta.max_seqlen_q, meta.max_seqlen_k, out=out,
+                              workspace=ws, stream=stream)
+        else:
+            B.hybrid_attn_fwd_two_launch(ds.q, ds.k_cache, ds.v_cache, ds.cu_seqlens_q,
+                                         ds.seqlens_k, ds.block_table, meta.max_seqlen_q,
+                                         meta.max_seqlen_k, out=out, workspace=ws,
+                                         two_streams=args.launch == "two-streams", stream=stream)
+
     def step():
         B.paged_kv_append(ds.key, ds.value, ds.slot_mapping, ds.k_cache, ds.v_cache, stream=stream)
-        B.hybrid_attn_fwd(ds.q, ds.k_cache, ds.v_cache, ds.cu_seqlens_q, ds.seqlens_k,
-                          ds.block_table, meta.max_seqlen_q, meta.max_seqlen_k, out=out,
-                          workspace=ws, stream=stream)
+        attention()
 
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
@@ -152,9 +163,7 @@ def main():
         e0.record(stream)
         B.paged_kv_append(ds.key, ds.value, ds.slot_mapping, ds.k_cache, ds.v_cache, stream=stream)
         e1.record(stream)
-        B.hybrid_attn_fwd(ds.q, ds.k_cache, ds.v_cache, ds.cu_seqlens_q, ds.seqlens_k,
-                          ds.block_table, meta.max_seqlen_q, meta.max_seqlen_k, out=out,
-                          workspace=ws, stream=stream)
+        attention()
         e2.record(stream)
     torch.cuda.synchronize()
     attn_ms = np.array([e1.elapsed_time(e2) for _, e1, e2 in ev])
@@ -196,9 +205,11 @@ def main():
         achieved = w["flops"] / (attn_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_tf,
                 "unit": "TFLOP/s", "frac": round(achieved / peak_tf, 4), "traffic": None}
-    roof["kernel"] = "hybrid_attn_fwd (plan_kernel + attn_kernel + combine_kernel, back to back)"
+    roof["kernel"] = ("hybrid_attn_fwd (plan_kernel + attn_kernel + combine_kernel, back to back)"
+                      if args.launch == "fused" else
+                      f"hybrid_attn_fwd_two_launch ({args.launch}: plan, chunk launch, decode launch, combine)")
     roof["avg_us"] = round(attn_us, 2)
-    roof["traffic"] = profiled_traffic(spec.name)
+    roof["traffic"] = profiled_traffic(spec.name) if args.launch == "fused" else None
 
     result = {
         "metric": METRIC, "value": round(us_step, 2), "unit": "us/step", "n_gpus": 1,
@@ -209,7 +220,7 @@ def main():
                    "num_heads": spec.num_heads, "num_kv_heads": spec.num_kv_heads,
                    "head_dim": spec.head_dim, "page_size": meta.page_size,
                    "max_seqlen_q": meta.max_seqlen_q, "max_seqlen_k": meta.max_seqlen_k,
-                   "seed": args.seed},
+                   "seed": args.seed, "launch": args.launch},
         "gpu_us_per_step": round(1e3 * gpu_ms / args.steps, 2),
         "tflops": round(w["flops"] / (us_step * 1e-6) / 1e12, 2),
         "kv_gbps": round(w["kv_bytes"] / (us_step * 1e-6) / 1e9, 1),

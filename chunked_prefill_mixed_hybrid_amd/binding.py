@@ -16,7 +16,8 @@ LIB_PATH = Path(__file__).resolve().parent / "libhybridattn.so"
 HA_OK, HA_ERR_INVALID_ARGUMENT, HA_ERR_UNSUPPORTED, HA_ERR_WORKSPACE_TOO_SMALL, HA_ERR_HIP = range(5)
 HA_DTYPE_F32, HA_DTYPE_BF16 = 0, 1
 
-EXPORTED = ("ha_status_string", "paged_kv_append", "hybrid_attn_workspace_size", "hybrid_attn_fwd")
+EXPORTED = ("ha_status_string", "paged_kv_append", "hybrid_attn_workspace_size", "hybrid_attn_fwd",
+            "hybrid_attn_fwd_two_launch")
 
 
 class HybridAttnError(RuntimeError):
@@ -47,6 +48,10 @@ def load(path: Path | str | None = None) -> ctypes.CDLL:
     lib.hybrid_attn_fwd.argtypes = ([vp, vp, vp, i32p, i32p, i32p, vp] + [i32] * 10 +
                                     [ctypes.c_float, ctypes.c_int, vp, ctypes.c_size_t, vp])
     lib.hybrid_attn_fwd.restype = ctypes.c_int
+    lib.hybrid_attn_fwd_two_launch.argtypes = ([vp, vp, vp, i32p, i32p, i32p, vp] + [i32] * 10 +
+                                               [ctypes.c_float, ctypes.c_int, vp, ctypes.c_size_t,
+                                                i32, vp])
+    lib.hybrid_attn_fwd_two_launch.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -117,26 +122,42 @@ def alloc_workspace(num_seqs, total_q, max_seqlen_k, num_heads, head_dim, device
 def hybrid_attn_fwd(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table, max_seqlen_q,
                     max_seqlen_k, out=None, sm_scale=None, workspace=None, stream=None):
     """One fused varlen paged attention forward (causal, right-aligned)."""
+    return _attn("hybrid_attn_fwd", q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table,
+                 max_seqlen_q, max_seqlen_k, out, sm_scale, workspace, stream, ())
+
+
+def hybrid_attn_fwd_two_launch(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table,
+                               max_seqlen_q, max_seqlen_k, out=None, sm_scale=None,
+                               workspace=None, two_streams=False, stream=None):
+    """The same computation with the chunk and decode roles in two launches
+    (back to back, or concurrently on two streams): a comparison baseline."""
+    return _attn("hybrid_attn_fwd_two_launch", q, k_cache, v_cache, cu_seqlens_q, seqlens_k,
+                 block_table, max_seqlen_q, max_seqlen_k, out, sm_scale, workspace, stream,
+                 (1 if two_streams else 0,))
+
+
+def _attn(fn, q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table, max_seqlen_q,
+          max_seqlen_k, out, sm_scale, workspace, stream, extra):
     import torch
     t, hq, d = q.shape
     nb, p, hkv, d2 = k_cache.shape
     if d2 != d or v_cache.shape != k_cache.shape:
-        raise ValueError("hybrid_attn_fwd: shape mismatch")
+        raise ValueError(f"{fn}: shape mismatch")
     b = seqlens_k.shape[0]
     if cu_seqlens_q.shape != (b + 1,) or block_table.dim() != 2 or block_table.shape[0] != b:
-        raise ValueError("hybrid_attn_fwd: metadata shapes")
+        raise ValueError(f"{fn}: metadata shapes")
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
         workspace = alloc_workspace(b, t, max_seqlen_k, hq, d, device=q.device)
     scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(d)
     dt = q.dtype
-    st = load().hybrid_attn_fwd(
+    st = getattr(load(), fn)(
         _dev(q, "q", dt), _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
         _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(seqlens_k, "seqlens_k", torch.int32),
         _dev(block_table, "block_table", torch.int32), _dev(out, "out", dt),
         b, t, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, p, nb, block_table.shape[1],
         scale, _dtype_code(q), _dev(workspace, "workspace", torch.uint8), workspace.numel(),
-        _stream(stream))
-    _check("hybrid_attn_fwd", st)
+        *extra, _stream(stream))
+    _check(fn, st)
     return out

@@ -51,14 +51,19 @@ size_t hybrid_attn_workspace_size(int32_t num_seqs, int32_t total_q, int32_t max
   return ha::ws_layout(num_seqs, total_q, max_seqlen_k, num_heads, head_dim).total;
 }
 
-ha_status hybrid_attn_fwd(const void* q, const void* k_cache, const void* v_cache,
-                          const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
-                          const int32_t* block_table, void* out, int32_t num_seqs,
-                          int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                          int32_t page_size, int32_t num_blocks, int32_t max_blocks_per_seq,
-                          float sm_scale, ha_dtype dtype, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the attention entry points; on HA_OK, L is ready to launch.
+ha_status attention_launch(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                           const int32_t* block_table, void* out, int32_t num_seqs,
+                           int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                           int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t page_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                           float sm_scale, ha_dtype dtype, void* workspace,
+                           size_t workspace_bytes, void* stream, int launch_mode) {
   if (num_seqs < 1 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_heads < 1 ||
       num_kv_heads < 1 || head_dim < 1 || page_size < 1 || num_blocks < 1 ||
       max_blocks_per_seq < 1)
@@ -95,10 +100,45 @@ ha_status hybrid_attn_fwd(const void* q, const void* k_cache, const void* v_cach
   L.max_blocks = max_blocks_per_seq;
   L.sm_scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf(static_cast<float>(head_dim));
   L.dtype = dtype == HA_DTYPE_F32 ? 0 : 1;
+  L.launch_mode = launch_mode;
   L.workspace = static_cast<unsigned char*>(workspace);
   L.ws = ws;
   L.stream = static_cast<hipStream_t>(stream);
   return ha::launch_attention(L) == hipSuccess ? HA_OK : HA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+ha_status hybrid_attn_fwd(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                          const int32_t* block_table, void* out, int32_t num_seqs,
+                          int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t page_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                          float sm_scale, ha_dtype dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return attention_launch(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table, out,
+                          num_seqs, total_q, max_seqlen_q, max_seqlen_k, num_heads, num_kv_heads,
+                          head_dim, page_size, num_blocks, max_blocks_per_seq, sm_scale, dtype,
+                          workspace, workspace_bytes, stream, ha::kLaunchFused);
+}
+
+ha_status hybrid_attn_fwd_two_launch(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                                     const int32_t* block_table, void* out, int32_t num_seqs,
+                                     int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                     int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t page_size, int32_t num_blocks,
+                                     int32_t max_blocks_per_seq, float sm_scale, ha_dtype dtype,
+                                     void* workspace, size_t workspace_bytes,
+                                     int32_t two_streams, void* stream) {
+  return attention_launch(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table, out,
+                          num_seqs, total_q, max_seqlen_q, max_seqlen_k, num_heads, num_kv_heads,
+                          head_dim, page_size, num_blocks, max_blocks_per_seq, sm_scale, dtype,
+                          workspace, workspace_bytes, stream,
+                          two_streams ? ha::kLaunchTwoStreams : ha::kLaunchSerial);
 }
 
 }  // extern "C"

@@ -30,6 +30,8 @@
 //         reduces the 16-lane partial dot products with a butterfly
 //         reduce-scatter, and keeps fp32 (m, l, acc) per lane.  Splits of a
 //         segment write partial (m, l, acc) rows that combine_kernel merges.
+#include <mutex>
+
 #include "ha_common.hpp"
 #include "ha_internal.hpp"
 
@@ -41,6 +43,9 @@ struct PlanArgs {
   const int32_t* sk;
   int num_seqs, total_q, max_q, max_k, max_blocks, num_heads, head_groups, parts_cap,
       target_items, grid, tiles_cap, chunk_slots_cap;
+  // workgroups that start on the chunk queues / on the decode queue (their first
+  // items are assigned statically, so the counters start past them)
+  int chunk_first_wgs, dec_first_wgs;
   // rough cost of one 64-key step of a chunk tile, in units of one decode
   // (key, head) pair: decides whether long chunk tiles are split along the keys
   int chunk_step_cost;
@@ -242,14 +247,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     a.hdr->bad_segments = s_bad;
     // the attention kernel hands out the first item of every workgroup statically:
     // chunk-first workgroup b takes item b / 8 of chunk group b % 8, decode-first
-    // workgroup b takes decode item b - half; the counters start past those items
-    const int half = (a.grid + 1) / 2;
+    // workgroup b takes decode item b - (chunk-first workgroups of its launch);
+    // the counters start past those items
+    const int cw = a.chunk_first_wgs;
     for (int x = 0; x < kXcdGroups; ++x) {
       const int items = chunk_group_heads(a.num_heads, x) * s_carry[0];
-      const int first = x < half ? (half - x + kXcdGroups - 1) / kXcdGroups : 0;
+      const int first = x < cw ? (cw - x + kXcdGroups - 1) / kXcdGroups : 0;
       a.hdr->chunk_counter[x] = static_cast<uint32_t>(min(items, first));
     }
-    a.hdr->dec_counter = static_cast<uint32_t>(min(s_carry[1], a.grid - half));
+    a.hdr->dec_counter = static_cast<uint32_t>(min(s_carry[1], a.dec_first_wgs));
   }
 }
 
@@ -270,6 +276,8 @@ struct MainArgs {
   const int32_t* part_prefix;
   float* partials;
   float* chunk_partials;  // [slot][head][128 rows][part_stride] of split chunk tiles
+  int roles;      // bit 0: this launch runs chunk items, bit 1: decode items
+  int chunk_wgs;  // workgroups of this launch that prefer the chunk queues (the first ones)
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -1183,15 +1191,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
     }
   }
   // Work distribution.  Decode splits come from one queue; chunk tiles from
-  // kXcdGroups queues (tiles of head h in group h % kXcdGroups).  The first half
-  // of the workgroups takes chunk tiles while any are left -- its own XCD's group
-  // first, then the others -- the second half decode splits; each falls back to
-  // the other kind when its own is empty, so both roles run side by side on every
-  // CU.  The first item of every workgroup is assigned statically (the planner
+  // kXcdGroups queues (tiles of head h in group h % kXcdGroups).  The first
+  // chunk_wgs workgroups (half of the grid in the fused launch) take chunk tiles
+  // while any are left -- their own XCD's group first, then the others -- the
+  // rest decode splits; each falls back to the other kind when its own is empty,
+  // so both roles run side by side on every CU.  A launch for one role only
+  // (roles) never opens the other kind's queues.  The first item of every workgroup is assigned statically (the planner
   // starts the counters past those items); afterwards the next item is claimed
   // with an atomic at the start of the current one, hiding the claim's latency.
-  const int half = (gridDim.x + 1) / 2;
-  const bool chunk_first = blockIdx.x < half;
+  const int half = a.chunk_wgs;
+  const bool chunk_first = static_cast<int>(blockIdx.x) < half;
   const int my_group = blockIdx.x % kXcdGroups;
   auto claim_chunk = [&]() -> int {
     if (!s_chunk_open) return kDone;
@@ -1233,8 +1242,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
     return it;
   };
   if (threadIdx.x == 0) {
-    s_chunk_open = (1u << kXcdGroups) - 1;
-    s_dec_open = 1;
+    s_chunk_open = (a.roles & 1) ? (1u << kXcdGroups) - 1 : 0u;
+    s_dec_open = (a.roles & 2) ? 1 : 0;
     const int rank = blockIdx.x / kXcdGroups;  // among chunk-first workgroups of this group
     if (chunk_first && rank < chunk_group_heads(a.num_heads, my_group) * n_tiles)
       s_next = (my_group << 24) | rank;
@@ -1444,8 +1453,34 @@ hipError_t occupancy(DeviceInfo& info, int dt, int di, int ds, const void* kerne
   return hipSuccess;
 }
 
+// Second stream and fork/join events of the two-stream baseline, per device,
+// created on first use (default priority).
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex lock;  // the record / wait / launch sequence of one call
+};
+SideStream g_side[64];
+
+hipError_t side_stream(int dev, SideStream*& out) {
+  SideStream& s = g_side[dev];
+  if (!s.stream) {
+    hipError_t e = hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&s.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&s.join, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+  }
+  out = &s;
+  return hipSuccess;
+}
+
+template <typename T, int D, bool kSplit>
+void launch_attn(const MainArgs& ma, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((attn_kernel<T, D, kSplit>), dim3(grid), dim3(kThreads), 0, st, ma);
+}
+
 template <typename T, int D>
-hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dt, int di) {
+hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
   // Chunk tiles may be split only when even the largest number of them the
   // bounds allow (tiles_cap per head) fills at most half of the resident
   // workgroups; every other step runs the instance without the split code.
@@ -1457,6 +1492,21 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dt, int di) {
   if (split_ok) {
     e = occupancy(info, dt, di, 1, reinterpret_cast<const void*>(attn_kernel<T, D, true>), grid);
     if (e != hipSuccess) return e;
+  }
+  SideStream* side = nullptr;
+  if (L.launch_mode == kLaunchTwoStreams) {
+    e = side_stream(dev, side);
+    if (e != hipSuccess) return e;
+  }
+  // workgroups per launch and how many of them start on the chunk queues
+  const int half = (grid + 1) / 2;
+  int chunk_first_wgs = half, dec_first_wgs = grid - half;  // fused
+  if (L.launch_mode == kLaunchSerial) {
+    chunk_first_wgs = grid;
+    dec_first_wgs = grid;
+  } else if (L.launch_mode == kLaunchTwoStreams) {
+    chunk_first_wgs = half;
+    dec_first_wgs = grid - half;
   }
   unsigned char* ws = L.workspace;
   PlanHeader* hdr = reinterpret_cast<PlanHeader*>(ws);
@@ -1471,8 +1521,8 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dt, int di) {
   const int chunk_step_cost = (sizeof(T) == 4 || D == 64) ? 192 : 128;
   PlanArgs pa{L.cu_seqlens_q, L.seqlens_k, L.num_seqs, L.total_q, L.max_seqlen_q, L.max_seqlen_k,
               L.max_blocks, L.num_heads, head_groups, L.ws.parts_cap, grid * kItemsPerSlot,
-              grid, L.ws.tiles_cap, split_ok ? L.ws.chunk_slots_cap : 0, chunk_step_cost, hdr,
-              tile_prefix, dec_prefix, part_prefix};
+              grid, L.ws.tiles_cap, split_ok ? L.ws.chunk_slots_cap : 0, chunk_first_wgs,
+              dec_first_wgs, chunk_step_cost, hdr, tile_prefix, dec_prefix, part_prefix};
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, L.stream, pa);
 
   MainArgs ma{L.q, L.k_cache, L.v_cache, L.out, L.cu_seqlens_q, L.seqlens_k, L.block_table,
@@ -1480,9 +1530,33 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dt, int di) {
               L.num_blocks, L.max_blocks, L.ws.part_stride, L.sm_scale * kLog2e, hdr,
               tile_prefix, dec_prefix, part_prefix,
               reinterpret_cast<float*>(ws + L.ws.partials),
-              reinterpret_cast<float*>(ws + L.ws.chunk_partials)};
-  if (split_ok) hipLaunchKernelGGL((attn_kernel<T, D, true>), dim3(grid), dim3(kThreads), 0, L.stream, ma);
-  else hipLaunchKernelGGL((attn_kernel<T, D, false>), dim3(grid), dim3(kThreads), 0, L.stream, ma);
+              reinterpret_cast<float*>(ws + L.ws.chunk_partials), 3, half};
+  auto attn = split_ok ? launch_attn<T, D, true> : launch_attn<T, D, false>;
+  if (L.launch_mode == kLaunchFused) {
+    attn(ma, grid, L.stream);
+  } else {
+    MainArgs mc = ma, md = ma;
+    mc.roles = 1;
+    md.roles = 2;
+    md.chunk_wgs = 0;
+    if (L.launch_mode == kLaunchSerial) {
+      mc.chunk_wgs = grid;
+      attn(mc, grid, L.stream);
+      attn(md, grid, L.stream);
+    } else {
+      mc.chunk_wgs = half;
+      std::lock_guard<std::mutex> g(side->lock);
+      e = hipEventRecord(side->fork, L.stream);
+      if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
+      if (e != hipSuccess) return e;
+      attn(mc, half, side->stream);
+      e = hipEventRecord(side->join, side->stream);
+      if (e != hipSuccess) return e;
+      attn(md, grid - half, L.stream);
+      e = hipStreamWaitEvent(L.stream, side->join, 0);
+      if (e != hipSuccess) return e;
+    }
+  }
   const int merge_blocks = split_ok ? kChunkMergeBlocks : 0;
   hipLaunchKernelGGL((combine_kernel<T, D>), dim3(L.num_seqs * head_groups + merge_blocks),
                      dim3(kThreads), 0, L.stream, ma);
@@ -1502,9 +1576,9 @@ hipError_t launch_attention(const AttnLaunch& L) {
     if (e != hipSuccess) return e;
   }
   if (L.dtype == 1) {
-    return L.head_dim == 128 ? run<bf16_t, 128>(L, info, 1, 1) : run<bf16_t, 64>(L, info, 1, 0);
+    return L.head_dim == 128 ? run<bf16_t, 128>(L, info, dev, 1, 1) : run<bf16_t, 64>(L, info, dev, 1, 0);
   }
-  return L.head_dim == 128 ? run<float, 128>(L, info, 0, 1) : run<float, 64>(L, info, 0, 0);
+  return L.head_dim == 128 ? run<float, 128>(L, info, dev, 0, 1) : run<float, 64>(L, info, dev, 0, 0);
 }
 
 }  // namespace ha

@@ -106,6 +106,11 @@ inline WsLayout ws_layout(int num_seqs, int total_q, int max_seqlen_k, int num_h
 }
 
 // ---- launchers ---------------------------------------------------------------------
+// How the chunk role and the decode role are launched: one fused persistent
+// kernel (the product path), or -- as a comparison baseline -- two launches,
+// one per role, back to back on the caller's stream or concurrently on two
+// streams with half of the resident workgroups each.
+constexpr int kLaunchFused = 0, kLaunchSerial = 1, kLaunchTwoStreams = 2;
 struct AttnLaunch {
   const void* q;
   const void* k_cache;
@@ -118,6 +123,7 @@ struct AttnLaunch {
   int num_heads, num_kv_heads, head_dim, num_blocks, max_blocks;
   float sm_scale;
   int dtype;  // 0 = f32, 1 = bf16
+  int launch_mode;  // kLaunchFused, kLaunchSerial or kLaunchTwoStreams
   unsigned char* workspace;
   WsLayout ws;
   hipStream_t stream;

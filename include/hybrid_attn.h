@@ -142,6 +142,34 @@ ha_status hybrid_attn_fwd(const void* q, const void* k_cache, const void* v_cach
                           float sm_scale, ha_dtype dtype, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/*
+ * hybrid_attn_fwd_two_launch -- the same computation as hybrid_attn_fwd, but
+ * with the chunk (prefill) role and the decode role in two separate kernel
+ * launches instead of one fused launch: the "separate prefill and decode
+ * kernels" alternative the kwkr.cn hybrid-attention article argues against
+ * (section on the hybrid batch).  It exists as a comparison baseline; results
+ * are bitwise equal to hybrid_attn_fwd for the same inputs and workspace size.
+ *
+ *   two_streams = 0  chunk launch, then decode launch, on `stream`
+ *   two_streams != 0 the chunk launch runs on a second stream the library
+ *                    creates on first use on each device (default priority),
+ *                    concurrently with the decode launch on `stream`; each
+ *                    launch gets half of the resident workgroups; `stream`
+ *                    waits for both before the merge.  The library keeps
+ *                    that stream and two events until the process ends.
+ *
+ * Other arguments, ownership and errors as for hybrid_attn_fwd.
+ */
+ha_status hybrid_attn_fwd_two_launch(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                                     const int32_t* block_table, void* out, int32_t num_seqs,
+                                     int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                     int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t page_size, int32_t num_blocks,
+                                     int32_t max_blocks_per_seq, float sm_scale, ha_dtype dtype,
+                                     void* workspace, size_t workspace_bytes,
+                                     int32_t two_streams, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

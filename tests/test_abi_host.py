@@ -51,15 +51,20 @@ def test_workspace_size_grows_with_bounds(lib):
 FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: every call below fails host-side
 
 
-def fwd(lib, **kw):
+def fwd(lib, entry="hybrid_attn_fwd", **kw):
     args = dict(q=FAKE, kc=FAKE, vc=FAKE, cu=FAKE, sk=FAKE, bt=FAKE, out=FAKE, B=3, T=1810,
                 mq=1808, mk=10000, H=2, Hkv=2, D=64, P=16, NB=644, MB=625, scale=0.125,
-                dt=B.HA_DTYPE_F32, ws=FAKE, wsb=1 << 30, stream=None)
+                dt=B.HA_DTYPE_F32, ws=FAKE, wsb=1 << 30)
     args.update(kw)
-    return lib.hybrid_attn_fwd(*args.values())
+    extra = [args.pop("two_streams")] if "two_streams" in args else []
+    if entry == "hybrid_attn_fwd_two_launch" and not extra:
+        extra = [0]
+    return getattr(lib, entry)(*args.values(), *extra, None)
 
 
-def test_fwd_argument_errors(lib):
+@pytest.mark.parametrize("entry", ["hybrid_attn_fwd", "hybrid_attn_fwd_two_launch"])
+def test_fwd_argument_errors(lib, entry):
+    fwd = lambda lib, **kw: globals()["fwd"](lib, entry, **kw)  # noqa: E731
     assert fwd(lib, Hkv=3) == B.HA_ERR_INVALID_ARGUMENT  # 2 % 3 != 0
     assert fwd(lib, mq=20000) == B.HA_ERR_INVALID_ARGUMENT  # max_seqlen_q > max_seqlen_k
     assert fwd(lib, B=0) == B.HA_ERR_INVALID_ARGUMENT
@@ -72,6 +77,9 @@ def test_fwd_argument_errors(lib):
     need = B.workspace_size(3, 1810, 10000, 2, 64)
     assert fwd(lib, wsb=need - 1) == B.HA_ERR_WORKSPACE_TOO_SMALL
     assert fwd(lib, T=0, wsb=need) == B.HA_OK  # nothing to do, nothing enqueued
+    if entry == "hybrid_attn_fwd_two_launch":
+        assert fwd(lib, T=0, wsb=need, two_streams=1) == B.HA_OK
+        assert fwd(lib, wsb=need - 1, two_streams=1) == B.HA_ERR_WORKSPACE_TOO_SMALL
 
 
 def app(lib, **kw):

@@ -102,6 +102,50 @@ def test_chunk_split(case):
     G.compare(G.to_f64(out2), ref, dt, f"split case {case}, second call")
 
 
+# ---------------------------------------------------------------- two-launch baseline
+# The chunk role and the decode role in separate launches (back to back, or on
+# two streams): the same plan and items as the fused launch, so the output is
+# bitwise the fused one.
+TWO_LAUNCH_CASES = [("sweep", 3), ("sweep", 6), ("sweep", 9), ("sweep", 11), ("split", 3),
+                    ("split", 5)]
+
+
+@pytest.mark.parametrize("two_streams", [False, True])
+@pytest.mark.parametrize("case", range(len(TWO_LAUNCH_CASES)))
+def test_two_launch_matches_fused(case, two_streams):
+    import torch
+    kind, idx = TWO_LAUNCH_CASES[case]
+    segs, hq, hkv, d, dt, seed = (SWEEP if kind == "sweep" else SPLIT_CASES)[idx]
+    spec, meta = W.custom_step(segs, hq, hkv, d, dt, seed=seed)
+    hs = W.host_values(spec, meta, seed=seed)
+    ds = _dev(hs)
+    ref, _, _ = G.oracle_full(ds, hs.k_cache, hs.v_cache)
+    G.note(f"two_launch {kind} case={idx} two_streams={two_streams} segs={segs}")
+    fused = G.gpu_step(ds)
+    two = B.hybrid_attn_fwd_two_launch(ds.q, ds.k_cache, ds.v_cache, ds.cu_seqlens_q, ds.seqlens_k,
+                                       ds.block_table, meta.max_seqlen_q, meta.max_seqlen_k,
+                                       two_streams=two_streams)
+    torch.cuda.synchronize()
+    assert torch.equal(two.view(torch.uint8), fused.view(torch.uint8))  # byte for byte
+    G.compare(G.to_f64(two), ref, dt, f"two-launch {kind} {idx}")
+
+
+def test_two_launch_config2_matches_fused():
+    import torch
+    spec, meta = W.make_step(2)
+    ds = W.device_values(spec, meta, seed=0)
+    G.note("two_launch config2 serial and two streams")
+    fused = G.gpu_step(ds)
+    for two_streams in (False, True):
+        two = B.hybrid_attn_fwd_two_launch(ds.q, ds.k_cache, ds.v_cache, ds.cu_seqlens_q,
+                                           ds.seqlens_k, ds.block_table, meta.max_seqlen_q,
+                                           meta.max_seqlen_k, two_streams=two_streams)
+        torch.cuda.synchronize()
+        assert torch.equal(two.view(torch.int16), fused.view(torch.int16)), two_streams
+    del ds
+    _free()
+
+
 # ---------------------------------------------------------------- full configs
 def test_config1_worked_example():
     spec, meta = W.make_step(1)
