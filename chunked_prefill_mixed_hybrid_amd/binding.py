@@ -37,6 +37,10 @@ def load(path: Path | str | None = None) -> ctypes.CDLL:
     p = Path(path) if path else LIB_PATH
     if not p.exists():
         raise RuntimeError(f"{p} not found: build it with `python -m chunked_prefill_mixed_hybrid_amd.build`")
+    # torch first: the library must bind to the HIP runtime torch loads (the
+    # ROCm torch wheel carries its own); loaded before it, the library would
+    # pull in a second runtime that cannot see torch's memory or streams
+    import torch  # noqa: F401
     lib = ctypes.CDLL(str(p))
     i32, vp, i32p = ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p
     lib.ha_status_string.argtypes = [ctypes.c_int]

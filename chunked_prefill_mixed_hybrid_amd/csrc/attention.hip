@@ -46,6 +46,7 @@ struct PlanArgs {
   // workgroups that start on the chunk queues / on the decode queue (their first
   // items are assigned statically, so the counters start past them)
   int chunk_first_wgs, dec_first_wgs;
+  int split_items;  // most chunk items splitting may create
   // rough cost of one 64-key step of a chunk tile, in units of one decode
   // (key, head) pair: decides whether long chunk tiles are split along the keys
   int chunk_step_cost;
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         const double longest = static_cast<double>(steps_max) * a.chunk_step_cost;
         if (longest > share) {
           long long want = static_cast<long long>(ceil(longest / share));
-          want = min(want, static_cast<long long>(a.grid) / (n_ct * a.num_heads));
+          want = min(want, static_cast<long long>(a.split_items) / (n_ct * a.num_heads));
           want = min(want, static_cast<long long>(kChunkSplitItems) / (n_ct * a.num_heads));
           want = min(want, static_cast<long long>(a.chunk_slots_cap) / n_ct);
           want = min(want, steps_max * 64 / kChunkSplitMinKeys);
@@ -1482,13 +1483,20 @@ void launch_attn(const MainArgs& ma, int grid, hipStream_t st) {
 template <typename T, int D>
 hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
   // Chunk tiles may be split only when even the largest number of them the
-  // bounds allow (tiles_cap per head) fills at most half of the resident
-  // workgroups; every other step runs the instance without the split code.
+  // bounds allow (tiles_cap per head) fills at most half of split_items; every
+  // other step runs the instance without the split code.
   int grid = 0;
   hipError_t e = occupancy(info, dt, di, 0, reinterpret_cast<const void*>(attn_kernel<T, D, false>), grid);
   if (e != hipSuccess) return e;
+  // For bf16, splitting pays only while it brings idle CUs into use: a second
+  // item on a CU shares its MFMA and LDS with the first (measured: a bf16 chunk
+  // of 8 tiles x 32 heads split in two ran 40 % slower), so splits stop at one
+  // item per CU.  fp32 tiles leave a CU underused with one workgroup (long
+  // fp32 MFMA chains): there they go up to one item per resident workgroup
+  // (worked example: 238 us against 308 us with one item per CU).
+  const int split_items = sizeof(T) == 4 ? grid : info.cus;
   const bool split_ok = L.ws.chunk_slots_cap >= 2 &&
-                        2LL * L.ws.tiles_cap * L.num_heads <= static_cast<long long>(grid);
+                        2LL * L.ws.tiles_cap * L.num_heads <= static_cast<long long>(split_items);
   if (split_ok) {
     e = occupancy(info, dt, di, 1, reinterpret_cast<const void*>(attn_kernel<T, D, true>), grid);
     if (e != hipSuccess) return e;
@@ -1522,7 +1530,8 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
   PlanArgs pa{L.cu_seqlens_q, L.seqlens_k, L.num_seqs, L.total_q, L.max_seqlen_q, L.max_seqlen_k,
               L.max_blocks, L.num_heads, head_groups, L.ws.parts_cap, grid * kItemsPerSlot,
               grid, L.ws.tiles_cap, split_ok ? L.ws.chunk_slots_cap : 0, chunk_first_wgs,
-              dec_first_wgs, chunk_step_cost, hdr, tile_prefix, dec_prefix, part_prefix};
+              dec_first_wgs, split_items, chunk_step_cost, hdr, tile_prefix, dec_prefix,
+              part_prefix};
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, L.stream, pa);
 
   MainArgs ma{L.q, L.k_cache, L.v_cache, L.out, L.cu_seqlens_q, L.seqlens_k, L.block_table,

@@ -1,0 +1,94 @@
+"""Tile-quantisation sweep: time of one mixed step as a function of the chunk
+length around multiples of the chunk tile (128 query rows).
+
+A token budget that overshoots a tile multiple by one token buys a whole extra
+query tile per head: the wangyu.me chunked-prefill page (section on how large
+the chunk should be) relays a measurement with 128-wide tiles where 257 tokens
+took about a third longer than 256, which is why step budgets get aligned to
+tile boundaries.  This sweep measures that effect for the fused kernel on MI355X: one
+chunk of length L at history H0, alone or packed with 30 decode segments of the
+bench workload's shape, 32 heads x 128, bf16, 16-token pages.
+
+    python -m chunked_prefill_mixed_hybrid_amd.sweep [--history 1536] [--reps 50]
+
+Prints one JSON line per (L, decodes) point and a table.  Synthetic inputs
+(seeded), as everywhere in this package.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+
+import numpy as np
+
+DEFAULT_LENGTHS = (896, 960, 1023, 1024, 1025, 1056, 1088, 1151, 1152, 1153, 1280)
+
+
+def _decodes(n: int, seed: int):
+    rng = np.random.default_rng(seed)
+    hist = rng.integers(512, 4096, n, endpoint=True)
+    return [(1, int(h) + 1) for h in hist]
+
+
+def time_step(segments, heads=32, head_dim=128, reps=50, warmup=5, seed=0):
+    """Median microseconds of hybrid_attn_fwd over `reps` calls (HIP events on
+    the stream the kernels run on) for one step of the given segments."""
+    import torch
+    from . import binding as B
+    from . import workload as W
+    spec, meta = W.custom_step(segments, heads, heads, head_dim, W.BF16, seed=seed)
+    ds = W.device_values(spec, meta, seed=seed)
+    out = torch.empty_like(ds.q)
+    ws = B.alloc_workspace(meta.num_seqs, meta.total_q, meta.max_seqlen_k, heads, head_dim)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        B.hybrid_attn_fwd(ds.q, ds.k_cache, ds.v_cache, ds.cu_seqlens_q, ds.seqlens_k,
+                          ds.block_table, meta.max_seqlen_q, meta.max_seqlen_k, out=out,
+                          workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        times.append((e0, e1))
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) for a, b in times]) * 1e3)
+    del ds, out, ws
+    torch.cuda.empty_cache()
+    return us
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--lengths", default=",".join(map(str, DEFAULT_LENGTHS)))
+    ap.add_argument("--history", type=int, default=1536, help="chunk history H0 (keys before it)")
+    ap.add_argument("--decodes", default="0,30", help="decode segments packed with the chunk")
+    ap.add_argument("--reps", type=int, default=50)
+    args = ap.parse_args(argv)
+    from . import binding as B
+    B.load()  # fail loudly if the HIP library is missing
+    rows = []
+    for nd in (int(x) for x in args.decodes.split(",")):
+        dec = _decodes(nd, seed=1)
+        for L in (int(x) for x in args.lengths.split(",")):
+            segs = [(L, args.history + L)] + dec
+            us = time_step(segs, reps=args.reps)
+            tiles = -(-L // 128)
+            row = {"chunk_len": L, "history": args.history, "decodes": nd, "tiles_per_head": tiles,
+                   "us": round(us, 2), "us_per_token": round(us / (L + nd), 4)}
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+    print(f"{'decodes':>7} {'L':>6} {'tiles':>5} {'us':>9} {'us/token':>9}")
+    for r in rows:
+        print(f"{r['decodes']:>7} {r['chunk_len']:>6} {r['tiles_per_head']:>5} {r['us']:>9.2f} "
+              f"{r['us_per_token']:>9.4f}")
+
+
+if __name__ == "__main__":
+    main()

@@ -47,6 +47,9 @@ SWEEP = [
     ([(128, 128), (256, 1024), (1, 1024)], 4, 4, 128, W.BF16, 10),
     ([(1, 4097), (33, 4129)], 64, 64, 128, W.BF16, 11),
     ([(5, 5), (1, 2000), (300, 2300)], 2, 1, 64, W.F32, 12),
+    # chunk lengths one past a tile multiple, as in the tile-quantisation sweep
+    ([(1025, 2561), (1, 3000), (1, 700)], 8, 8, 128, W.BF16, 13),
+    ([(1153, 1153), (1, 64)], 4, 4, 128, W.BF16, 14),
 ]
 
 
