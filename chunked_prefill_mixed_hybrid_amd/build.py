@@ -2,8 +2,9 @@
 
     python -m chunked_prefill_mixed_hybrid_amd.build
 
-Each .hip translation unit is compiled with hipcc for gfx950 only, then linked
-into one shared library exporting the C ABI of include/hybrid_attn.h.
+Each .hip translation unit is compiled with hipcc for gfx950 only, the host-only
+C++ (the step generator) with g++, then everything is linked into one shared
+library exporting the C ABI of include/hybrid_attn.h and include/ha_scheduler.h.
 """
 from __future__ import annotations
 
@@ -19,6 +20,7 @@ CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIB = PKG / "libhybridattn.so"
 SOURCES = ["api.hip", "attention.hip", "kv_append.hip"]
+HOST_SOURCES = ["scheduler.cpp"]  # host-only C++ (no device code), built with the host compiler
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -53,6 +55,11 @@ def build(verbose: bool = False) -> Path:
         objs.append(obj)
         cmds.append([hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", str(CSRC / src),
                      "-o", str(obj)])
+    for src in HOST_SOURCES:
+        obj = obj_dir / (Path(src).stem + ".o")
+        objs.append(obj)
+        cmds.append(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}",
+                     "-c", str(CSRC / src), "-o", str(obj)])
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out:

@@ -10,9 +10,12 @@ chunk of length L at history H0, alone or packed with 30 decode segments of the
 bench workload's shape, 32 heads x 128, bf16, 16-token pages.
 
     python -m chunked_prefill_mixed_hybrid_amd.sweep [--history 1536] [--reps 50]
+    python -m chunked_prefill_mixed_hybrid_amd.sweep trace
 
-Prints one JSON line per (L, decodes) point and a table.  Synthetic inputs
-(seeded), as everywhere in this package.
+The first prints one JSON line per (L, decodes) point and a table; `trace`
+runs a 64-request trace through the token-budget step generator (one JSON
+line: steps, tokens/s, per-step times, fraction of the per-step rooflines).
+Synthetic inputs (seeded), as everywhere in this package.
 """
 from __future__ import annotations
 
@@ -64,8 +67,74 @@ def time_step(segments, heads=32, head_dim=128, reps=50, warmup=5, seed=0):
     return us
 
 
+def trace(num_requests=64, budget=2048, threshold=0, prompt=(256, 4096), new_tokens=(16, 128),
+          heads=32, head_dim=128, seed=0):
+    """A request trace scheduled by the token-budget step generator and run step
+    by step (paged_kv_append + hybrid_attn_fwd on one page pool): per-step GPU
+    time (HIP events, scheduling and metadata uploads outside), tokens and
+    algorithmic bytes.  Values are random; every request arrives at the start."""
+    import torch
+    from . import binding as B
+    from .scheduler import StepScheduler
+    rng = np.random.default_rng(seed)
+    plens = rng.integers(prompt[0], prompt[1], num_requests, endpoint=True)
+    gens = rng.integers(new_tokens[0], new_tokens[1], num_requests, endpoint=True)
+    page = 16
+    nb = int(sum(-(-int(p + g) // page) for p, g in zip(plens, gens))) + 64
+    mb = int(max(-(-int(p + g) // page) for p, g in zip(plens, gens)))
+    s = StepScheduler(budget, nb, mb, long_prefill_token_threshold=threshold,
+                      max_seqs=num_requests)
+    for r, (p, g) in enumerate(zip(plens, gens)):
+        s.add(r, int(p), int(g))
+    kc = torch.zeros((nb, page, heads, head_dim), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    ws = B.alloc_workspace(num_requests, budget, mb * page, heads, head_dim)
+    stream = torch.cuda.current_stream()
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()  # noqa: E731
+    steps = []
+    while (st := s.next_step()) is not None:
+        t = st.total_q
+        q = torch.randn((t, heads, head_dim), device="cuda").to(torch.bfloat16)
+        k = torch.randn((t, heads, head_dim), device="cuda").to(torch.bfloat16)
+        v = torch.randn((t, heads, head_dim), device="cuda").to(torch.bfloat16)
+        sm, cu, sk, bt = i32(st.slot_mapping), i32(st.cu_seqlens_q), i32(st.seqlens_k), i32(st.block_table)
+        out = torch.empty_like(q)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        B.paged_kv_append(k, v, sm, kc, vc, stream=stream)
+        B.hybrid_attn_fwd(q, kc, vc, cu, sk, bt, st.max_seqlen_q, st.max_seqlen_k, out=out,
+                          workspace=ws, stream=stream)
+        e1.record(stream)
+        lq = np.diff(st.cu_seqlens_q).astype(np.int64)
+        lk = st.seqlens_k.astype(np.int64)
+        kv_bytes = 2.0 * head_dim * heads * 2 * float(lk.sum())
+        bytes_ = kv_bytes + 2.0 * head_dim * heads * (2 + 4) * t + 4.0 * (
+            float(((lk + 15) // 16).sum()) + 2 * len(lk) + 1 + t)
+        vis = lq * (lk - lq) + lq * (lq + 1) // 2
+        flops = 4.0 * head_dim * heads * float(vis.sum())
+        steps.append((e0, e1, t, st.num_seqs, st.num_decodes, bytes_, flops))
+        s.complete()
+    torch.cuda.synchronize()
+    rows = []
+    for e0, e1, t, b, nd, by, fl in steps:
+        us = e0.elapsed_time(e1) * 1e3
+        roof = max(by / 8e12, fl / 2.5e15) * 1e6
+        rows.append((us, t, b, nd, roof))
+    a = np.array(rows)
+    res = {"requests": num_requests, "budget": budget, "steps": len(rows),
+           "tokens": int(a[:, 1].sum()), "gpu_ms": round(float(a[:, 0].sum()) / 1e3, 2),
+           "tokens_per_s": round(float(a[:, 1].sum() / (a[:, 0].sum() * 1e-6)), 1),
+           "us_per_step_median": round(float(np.median(a[:, 0])), 1),
+           "us_per_step_p90": round(float(np.percentile(a[:, 0], 90)), 1),
+           "frac_of_step_rooflines": round(float(a[:, 4].sum() / a[:, 0].sum()), 4),
+           "mixed_steps": int(((a[:, 3] > 0) & (a[:, 3] < a[:, 2])).sum()),
+           "decode_only_steps": int((a[:, 3] == a[:, 2]).sum())}
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("mode", nargs="?", default="tiles", choices=["tiles", "trace"])
     ap.add_argument("--lengths", default=",".join(map(str, DEFAULT_LENGTHS)))
     ap.add_argument("--history", type=int, default=1536, help="chunk history H0 (keys before it)")
     ap.add_argument("--decodes", default="0,30", help="decode segments packed with the chunk")
@@ -73,6 +142,9 @@ def main(argv=None):
     args = ap.parse_args(argv)
     from . import binding as B
     B.load()  # fail loudly if the HIP library is missing
+    if args.mode == "trace":
+        print(json.dumps(trace()), flush=True)
+        return
     rows = []
     for nd in (int(x) for x in args.decodes.split(",")):
         dec = _decodes(nd, seed=1)

@@ -207,6 +207,29 @@ def host_values(spec: StepSpec, meta: StepMeta, seed: int = 0, poison: bool = Tr
     return HostStep(spec, meta, q, key, value, kc, vc)
 
 
+def request_values(request_id: int, n_tokens: int, num_heads: int, num_kv_heads: int,
+                   head_dim: int, dtype: str, seed: int = 0):
+    """q [n, Hq, D], k and v [n, Hkv, D] of every token of one request (prompt and
+    generated tokens), drawn per request so that whichever step schedules a
+    token sees the same bytes."""
+    rng = np.random.default_rng([seed, 2, int(request_id)])
+    q = _store(rng.standard_normal((n_tokens, num_heads, head_dim), dtype=np.float32), dtype)
+    k = _store(rng.standard_normal((n_tokens, num_kv_heads, head_dim), dtype=np.float32), dtype)
+    v = _store(rng.standard_normal((n_tokens, num_kv_heads, head_dim), dtype=np.float32), dtype)
+    return q, k, v
+
+
+def step_tokens(request_ids, first_pos, cu_seqlens_q, values):
+    """(request, position) of every query row of a scheduled step, and the q /
+    key / value rows gathered from per-request `values` {id: (q, k, v)}."""
+    n = np.diff(np.asarray(cu_seqlens_q))
+    rows = [(int(r), int(f) + i) for r, f, c in zip(request_ids, first_pos, n) for i in range(c)]
+    q = np.stack([values[r][0][p] for r, p in rows])
+    k = np.stack([values[r][1][p] for r, p in rows])
+    v = np.stack([values[r][2][p] for r, p in rows])
+    return rows, q, k, v
+
+
 def torch_dtype(dtype: str):
     import torch
     return torch.float32 if dtype == F32 else torch.bfloat16

@@ -9,7 +9,7 @@ import pytest
 
 from chunked_prefill_mixed_hybrid_amd import binding as B
 
-HEADER = Path(__file__).resolve().parent.parent / "include" / "hybrid_attn.h"
+HEADERS = sorted((Path(__file__).resolve().parent.parent / "include").glob("*.h"))
 
 
 @pytest.fixture(scope="module")
@@ -21,12 +21,17 @@ def lib():
 
 
 def declared_functions():
-    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?([a-z_0-9]+)\(", text, re.M)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", h.read_text(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?([a-z_0-9]+)\(", text, re.M))
+    return sorted(names)
 
 
-def test_header_declares_the_abi():
-    assert declared_functions() == sorted(B.EXPORTED)
+def test_headers_declare_the_abi():
+    from chunked_prefill_mixed_hybrid_amd import scheduler
+    assert len(HEADERS) == 2
+    assert declared_functions() == sorted(B.EXPORTED + scheduler.EXPORTED)
 
 
 def test_every_declared_symbol_is_exported(lib):
