@@ -17,7 +17,7 @@ HA_OK, HA_ERR_INVALID_ARGUMENT, HA_ERR_UNSUPPORTED, HA_ERR_WORKSPACE_TOO_SMALL, 
 HA_DTYPE_F32, HA_DTYPE_BF16 = 0, 1
 
 EXPORTED = ("ha_status_string", "paged_kv_append", "hybrid_attn_workspace_size", "hybrid_attn_fwd",
-            "hybrid_attn_fwd_two_launch")
+            "hybrid_attn_fwd_two_launch", "varlen_attn_fwd")
 
 
 class HybridAttnError(RuntimeError):
@@ -56,6 +56,9 @@ def load(path: Path | str | None = None) -> ctypes.CDLL:
                                                [ctypes.c_float, ctypes.c_int, vp, ctypes.c_size_t,
                                                 i32, vp])
     lib.hybrid_attn_fwd_two_launch.restype = ctypes.c_int
+    lib.varlen_attn_fwd.argtypes = ([vp, vp, vp, i32p, i32p, vp] + [i32] * 8 +
+                                    [ctypes.c_float, ctypes.c_int, vp, ctypes.c_size_t, vp])
+    lib.varlen_attn_fwd.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -138,6 +141,34 @@ def hybrid_attn_fwd_two_launch(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, blo
     return _attn("hybrid_attn_fwd_two_launch", q, k_cache, v_cache, cu_seqlens_q, seqlens_k,
                  block_table, max_seqlen_q, max_seqlen_k, out, sm_scale, workspace, stream,
                  (1 if two_streams else 0,))
+
+
+def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, out=None,
+                    sm_scale=None, workspace=None, stream=None):
+    """The same attention over K/V packed per segment: segment b's keys are rows
+    cu_seqlens_k[b] .. cu_seqlens_k[b+1] - 1 of k and v [total_k, Hkv, D]."""
+    import torch
+    t, hq, d = q.shape
+    tk, hkv, d2 = k.shape
+    if d2 != d or v.shape != k.shape:
+        raise ValueError("varlen_attn_fwd: shape mismatch")
+    b = cu_seqlens_k.shape[0] - 1
+    if cu_seqlens_q.shape != (b + 1,):
+        raise ValueError("varlen_attn_fwd: metadata shapes")
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = alloc_workspace(b, t, max_seqlen_k, hq, d, device=q.device)
+    scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(d)
+    dt = q.dtype
+    st = load().varlen_attn_fwd(
+        _dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+        _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32), _dev(out, "out", dt),
+        b, t, tk, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, scale, _dtype_code(q),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
+    _check("varlen_attn_fwd", st)
+    return out
 
 
 def _attn(fn, q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table, max_seqlen_q,

@@ -58,7 +58,8 @@ namespace {
 // Checks shared by the attention entry points; on HA_OK, L is ready to launch.
 ha_status attention_launch(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
-                           const int32_t* block_table, void* out, int32_t num_seqs,
+                           const int32_t* block_table, const int32_t* cu_seqlens_k,
+                           int32_t total_k, void* out, int32_t num_seqs,
                            int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                            int32_t page_size, int32_t num_blocks, int32_t max_blocks_per_seq,
@@ -73,8 +74,8 @@ ha_status attention_launch(const void* q, const void* k_cache, const void* v_cac
     return HA_ERR_INVALID_ARGUMENT;
   if (static_cast<long long>(num_blocks) * page_size > 0x7fffffffLL) return HA_ERR_INVALID_ARGUMENT;
   if (!supported_shape(head_dim, page_size, dtype)) return HA_ERR_UNSUPPORTED;
-  if (!cu_seqlens_q || !seqlens_k || !block_table || !k_cache || !v_cache || !workspace)
-    return HA_ERR_INVALID_ARGUMENT;
+  if (!cu_seqlens_q || !k_cache || !v_cache || !workspace) return HA_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens_k ? total_k < 0 : (!seqlens_k || !block_table)) return HA_ERR_INVALID_ARGUMENT;
   if (total_q > 0 && (!q || !out)) return HA_ERR_INVALID_ARGUMENT;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return HA_ERR_INVALID_ARGUMENT;
   const ha::WsLayout ws = ha::ws_layout(num_seqs, total_q, max_seqlen_k, num_heads, head_dim);
@@ -88,6 +89,8 @@ ha_status attention_launch(const void* q, const void* k_cache, const void* v_cac
   L.cu_seqlens_q = cu_seqlens_q;
   L.seqlens_k = seqlens_k;
   L.block_table = block_table;
+  L.cu_seqlens_k = cu_seqlens_k;
+  L.total_k = total_k;
   L.out = out;
   L.num_seqs = num_seqs;
   L.total_q = total_q;
@@ -119,10 +122,10 @@ ha_status hybrid_attn_fwd(const void* q, const void* k_cache, const void* v_cach
                           int32_t page_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                           float sm_scale, ha_dtype dtype, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  return attention_launch(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table, out,
-                          num_seqs, total_q, max_seqlen_q, max_seqlen_k, num_heads, num_kv_heads,
-                          head_dim, page_size, num_blocks, max_blocks_per_seq, sm_scale, dtype,
-                          workspace, workspace_bytes, stream, ha::kLaunchFused);
+  return attention_launch(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table, nullptr, 0,
+                          out, num_seqs, total_q, max_seqlen_q, max_seqlen_k, num_heads,
+                          num_kv_heads, head_dim, page_size, num_blocks, max_blocks_per_seq,
+                          sm_scale, dtype, workspace, workspace_bytes, stream, ha::kLaunchFused);
 }
 
 ha_status hybrid_attn_fwd_two_launch(const void* q, const void* k_cache, const void* v_cache,
@@ -134,11 +137,27 @@ ha_status hybrid_attn_fwd_two_launch(const void* q, const void* k_cache, const v
                                      int32_t max_blocks_per_seq, float sm_scale, ha_dtype dtype,
                                      void* workspace, size_t workspace_bytes,
                                      int32_t two_streams, void* stream) {
-  return attention_launch(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table, out,
-                          num_seqs, total_q, max_seqlen_q, max_seqlen_k, num_heads, num_kv_heads,
-                          head_dim, page_size, num_blocks, max_blocks_per_seq, sm_scale, dtype,
-                          workspace, workspace_bytes, stream,
+  return attention_launch(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table, nullptr, 0,
+                          out, num_seqs, total_q, max_seqlen_q, max_seqlen_k, num_heads,
+                          num_kv_heads, head_dim, page_size, num_blocks, max_blocks_per_seq,
+                          sm_scale, dtype, workspace, workspace_bytes, stream,
                           two_streams ? ha::kLaunchTwoStreams : ha::kLaunchSerial);
+}
+
+ha_status varlen_attn_fwd(const void* q, const void* k, const void* v,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* out,
+                          int32_t num_seqs, int32_t total_q, int32_t total_k,
+                          int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_heads,
+                          int32_t num_kv_heads, int32_t head_dim, float sm_scale, ha_dtype dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cu_seqlens_k) return HA_ERR_INVALID_ARGUMENT;
+  // the paged kernels read a packed buffer as pages of 16 rows starting at each
+  // segment's first row (identity block table)
+  const int32_t pages = max_seqlen_k > 0 ? (max_seqlen_k + ha::kPage - 1) / ha::kPage : 1;
+  return attention_launch(q, k, v, cu_seqlens_q, nullptr, nullptr, cu_seqlens_k, total_k, out,
+                          num_seqs, total_q, max_seqlen_q, max_seqlen_k, num_heads, num_kv_heads,
+                          head_dim, ha::kPage, 1, pages, sm_scale, dtype, workspace,
+                          workspace_bytes, stream, ha::kLaunchFused);
 }
 
 }  // extern "C"

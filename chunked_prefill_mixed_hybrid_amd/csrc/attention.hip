@@ -50,6 +50,11 @@ struct PlanArgs {
   // rough cost of one 64-key step of a chunk tile, in units of one decode
   // (key, head) pair: decides whether long chunk tiles are split along the keys
   int chunk_step_cost;
+  // contiguous K/V: segment b's keys are rows cu_k[b] .. cu_k[b+1] of a buffer of
+  // total_k rows; the planner writes Lk_b into sk_out for the other kernels
+  const int32_t* cu_k;
+  int total_k;
+  int32_t* sk_out;
   PlanHeader* hdr;
   int32_t* tile_prefix;
   int32_t* dec_prefix;
@@ -63,8 +68,15 @@ constexpr int kPlanThreads = 1024;
 __device__ __forceinline__ bool plan_segment(const PlanArgs& a, int b, int& lq, int& lk) {
   const int c0 = a.cu[b], c1 = a.cu[b + 1];
   lq = c1 - c0;
-  lk = a.sk[b];
-  return c0 >= 0 && c1 >= c0 && c1 <= a.total_q && lq <= lk && lk <= a.max_k &&
+  bool rows_ok = true;
+  if (a.cu_k) {
+    const int k0 = a.cu_k[b], k1 = a.cu_k[b + 1];
+    lk = k1 - k0;
+    rows_ok = k0 >= 0 && k1 <= a.total_k;
+  } else {
+    lk = a.sk[b];
+  }
+  return rows_ok && c0 >= 0 && c1 >= c0 && c1 <= a.total_q && lq <= lk && lk <= a.max_k &&
          lq <= a.max_q && ((lk + kPage - 1) / kPage) <= a.max_blocks;
 }
 
@@ -195,6 +207,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     if (b < a.num_seqs) {
       int lq = my_lq, lk = my_lk;
       if (base > 0 && !plan_segment(a, b, lq, lk)) lq = -1;
+      if (a.sk_out) a.sk_out[b] = lq < 0 ? 0 : lk;
       if (lq < 0) {
         atomicAdd(&s_bad, 1);
       } else if (lq >= 2) {
@@ -277,6 +290,7 @@ struct MainArgs {
   const int32_t* part_prefix;
   float* partials;
   float* chunk_partials;  // [slot][head][128 rows][part_stride] of split chunk tiles
+  const int32_t* cu_k;  // contiguous K/V: first row of each segment's keys (else null)
   int roles;      // bit 0: this launch runs chunk items, bit 1: decode items
   int chunk_wgs;  // workgroups of this launch that prefer the chunk queues (the first ones)
 };
@@ -300,6 +314,35 @@ __device__ __forceinline__ int find_segment(const int32_t* prefix, int n, int x)
 // registers and V^T is read from LDS with one 16-byte load per MFMA.
 __device__ __forceinline__ int key_perm(int r) {
   return ((r >> 4) << 4) | (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 2) | (r & 3);
+}
+
+// Where the keys of a segment live.  Paged: key j is in page
+// block_table[seg][j / 16] of the pool.  Contiguous (varlen_attn_fwd): the
+// segment's keys are rows cu_k[seg] .. of a packed [total_k, Hkv, D] buffer;
+// a run of 16 keys then starts at row cu_k[seg] + 16 * (j / 16).  A "page"
+// below is a block id (paged) or that first row (contiguous), -1 for none, and
+// page_base turns it into the address of the run's first key, so both layouts
+// share every role's code.
+template <bool kContig>
+__device__ __forceinline__ int segment_page(const_i32_t* btrow, int row0, int idx, int last_page,
+                                            int num_blocks) {
+  if constexpr (kContig) {
+    return idx <= last_page ? row0 + idx * kPage : -1;
+  } else {
+    const int id = btrow[min(idx, last_page)];  // scalar load, always inside the row
+    return (idx <= last_page && static_cast<unsigned>(id) < static_cast<unsigned>(num_blocks)) ? id : -1;
+  }
+}
+template <bool kContig>
+__device__ __forceinline__ unsigned char* page_base(const void* pool, int page, uint32_t slot_bytes,
+                                                    uint32_t page_bytes) {
+  unsigned char* p = const_cast<unsigned char*>(static_cast<const unsigned char*>(pool));
+  return p + static_cast<size_t>(page < 0 ? 0 : page) * (kContig ? slot_bytes : page_bytes);
+}
+template <bool kContig>
+__device__ __forceinline__ int segment_row0(const MainArgs& a, int seg) {
+  if constexpr (kContig) return a.cu_k[seg];
+  else return 0;
 }
 
 // XOR swizzle (in 16-byte chunks of 8 keys) of row d of the transposed V tile.
@@ -362,8 +405,9 @@ __device__ __forceinline__ void chunk_store_partial(const MainArgs& a, int seg, 
 }
 
 // ---------------------------------------------------------------- chunk role, bf16
-// kSplit: the tile is one of nsplit key ranges (else nsplit == 1, split == 0)
-template <int D, bool kSplit>
+// kSplit: the tile is one of nsplit key ranges (else nsplit == 1, split == 0);
+// kContig: keys in a packed buffer instead of pages
+template <int D, bool kSplit, bool kContig>
 __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, int split, int nsplit,
                                 unsigned char* smem) {
   if constexpr (!kSplit) {
@@ -417,24 +461,20 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, int
   const uint32_t slot_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 2;
   const uint32_t page_bytes = slot_bytes * kPage;
   const uint32_t head_off = static_cast<uint32_t>(kvh) * D * 2;
-  unsigned char* kpool = const_cast<unsigned char*>(static_cast<const unsigned char*>(a.kc));
-  unsigned char* vpool = const_cast<unsigned char*>(static_cast<const unsigned char*>(a.vc));
+  const int krow0 = segment_row0<kContig>(a, seg);  // first key row (contiguous K/V)
   const int vc_ = tid % CPR, vkg = tid / CPR;  // V transpose: chunk and key group of this thread
   u32x4_t kreg[KLOADS], vreg[VKG];
   // page ids of a tile (scalar loads); -1 past kend or outside the pool
   auto tile_ids = [&](int k0, int (&ids)[4]) {
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      const int idx = (k0 >> 4) + pp;
-      const int id = btrow[min(idx, last_page)];
-      ids[pp] = (idx <= last_page && static_cast<unsigned>(id) < static_cast<unsigned>(a.num_blocks)) ? id : -1;
-    }
+    for (int pp = 0; pp < 4; ++pp)
+      ids[pp] = segment_page<kContig>(btrow, krow0, (k0 >> 4) + pp, last_page, a.num_blocks);
   };
   auto issue_tile = [&](int k0, const int (&ids)[4]) {
-    auto rsrc = [&](unsigned char* pool, int pidx) {  // pidx uniform: select, no indexed array
+    auto rsrc = [&](const void* pool, int pidx) {  // pidx uniform: select, no indexed array
       const int id = pidx == 0 ? ids[0] : pidx == 1 ? ids[1] : pidx == 2 ? ids[2] : ids[3];
-      return __builtin_amdgcn_make_buffer_rsrc(pool + static_cast<size_t>(id < 0 ? 0 : id) * page_bytes,
-                                               0, id < 0 ? 0 : static_cast<int>(page_bytes),
+      return __builtin_amdgcn_make_buffer_rsrc(page_base<kContig>(pool, id, slot_bytes, page_bytes), 0,
+                                               id < 0 ? 0 : static_cast<int>(page_bytes),
                                                kRawBufferWord3);
     };
 #pragma unroll
@@ -443,10 +483,10 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, int
       const uint32_t off = (k0 + key < kb1)
                                ? (key & 15) * slot_bytes + head_off + (tid % CPR) * 16
                                : kOffsetOutOfRange;
-      const auto rs = rsrc(kpool, (it * kThreads + w * kWave) / (16 * CPR));
+      const auto rs = rsrc(a.kc, (it * kThreads + w * kWave) / (16 * CPR));
       kreg[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
     }
-    const auto rs = rsrc(vpool, w);
+    const auto rs = rsrc(a.vc, w);
 #pragma unroll
     for (int t = 0; t < VKG; ++t) {
       const int key = vkg * VKG + t;
@@ -611,7 +651,7 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, int
 }
 
 // ---------------------------------------------------------------- chunk role, fp32
-template <int D, bool kSplit>
+template <int D, bool kSplit, bool kContig>
 __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, int split, int nsplit,
                                unsigned char* smem) {
   if constexpr (!kSplit) {
@@ -660,15 +700,13 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, int 
   const uint32_t slot_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 4;
   const uint32_t page_bytes = slot_bytes * kPage;
   const uint32_t head_off = static_cast<uint32_t>(kvh) * D * 4;
-  unsigned char* kpool = const_cast<unsigned char*>(static_cast<const unsigned char*>(a.kc));
-  unsigned char* vpool = const_cast<unsigned char*>(static_cast<const unsigned char*>(a.vc));
+  const int krow0 = segment_row0<kContig>(a, seg);  // first key row (contiguous K/V)
   u32x4_t kreg[LOADS], vreg[LOADS];
-  auto page_rsrc = [&](unsigned char* pool, int k0, int pidx) {
-    const int idx = (k0 >> 4) + pidx;
-    const int id = btrow[min(idx, last_page)];
-    const bool ok = idx <= last_page && static_cast<unsigned>(id) < static_cast<unsigned>(a.num_blocks);
-    return __builtin_amdgcn_make_buffer_rsrc(pool + static_cast<size_t>(ok ? id : 0) * page_bytes, 0,
-                                             ok ? static_cast<int>(page_bytes) : 0, kRawBufferWord3);
+  auto page_rsrc = [&](const void* pool, int k0, int pidx) {
+    const int id = segment_page<kContig>(btrow, krow0, (k0 >> 4) + pidx, last_page, a.num_blocks);
+    return __builtin_amdgcn_make_buffer_rsrc(page_base<kContig>(pool, id, slot_bytes, page_bytes), 0,
+                                             id >= 0 ? static_cast<int>(page_bytes) : 0,
+                                             kRawBufferWord3);
   };
   auto issue_tile = [&](int k0) {
 #pragma unroll
@@ -678,8 +716,8 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, int 
       const uint32_t off = (k0 + key < kb1)
                                ? (key & 15) * slot_bytes + head_off + (tid % CPR) * 16
                                : kOffsetOutOfRange;
-      const auto kr = page_rsrc(kpool, k0, pidx);
-      const auto vr = page_rsrc(vpool, k0, pidx);
+      const auto kr = page_rsrc(a.kc, k0, pidx);
+      const auto vr = page_rsrc(a.vc, k0, pidx);
       kreg[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
       vreg[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0));
     }
@@ -826,7 +864,7 @@ __device__ __forceinline__ void store_row(T* p, const float* v) {
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool kContig>
 __device__ void decode_item(const MainArgs& a, int seg, int j, int split_keys) {
   constexpr int EPL = D / 16;  // channels per lane
   using Frag = RowFrag<T, EPL>;
@@ -845,6 +883,8 @@ __device__ void decode_item(const MainArgs& a, int seg, int j, int split_keys) {
   const size_t slot_elems = static_cast<size_t>(a.num_kv_heads) * D;
   const T* kbase = static_cast<const T*>(a.kc) + static_cast<size_t>(kvh) * D + c * EPL;
   const T* vbase = static_cast<const T*>(a.vc) + static_cast<size_t>(kvh) * D + c * EPL;
+  const int row0 = segment_row0<kContig>(a, seg);
+  const int nb_ok = kContig ? 0x7fffffff : a.num_blocks;  // contiguous: any first row >= 0
 
   float qv[EPL];
   {
@@ -860,14 +900,15 @@ __device__ void decode_item(const MainArgs& a, int seg, int j, int split_keys) {
   for (int kb = kbeg; kb < kfin; kb += 64) {
     int pages[4];
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) pages[pp] = (kb + pp * 16 < kfin) ? btrow[(kb >> 4) + pp] : -1;
+    for (int pp = 0; pp < 4; ++pp)
+      pages[pp] = (kb + pp * 16 < kfin) ? (kContig ? row0 + kb + pp * 16 : btrow[(kb >> 4) + pp]) : -1;
     Frag kf[16], vf[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int pg = pages[u >> 2];
       const bool ok = (kb + 4 * u + r < kfin) &&
-                      static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_blocks);
-      const size_t off = (static_cast<size_t>(ok ? pg : 0) * kPage + 4 * (u & 3) + r) * slot_elems;
+                      static_cast<unsigned>(pg) < static_cast<unsigned>(nb_ok);
+      const size_t off = (static_cast<size_t>(ok ? pg : 0) * (kContig ? 1 : kPage) + 4 * (u & 3) + r) * slot_elems;
       if (ok) kf[u].load(kbase + off); else kf[u].zero();
       if constexpr (!kLateV) {
         if (ok) vf[u].load(vbase + off); else vf[u].zero();
@@ -906,8 +947,8 @@ __device__ void decode_item(const MainArgs& a, int seg, int j, int split_keys) {
       for (int u = 0; u < 16; ++u) {
         const int pg = pages[u >> 2];
         const bool ok = (kb + 4 * u + r < kfin) &&
-                        static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_blocks);
-        const size_t off = (static_cast<size_t>(ok ? pg : 0) * kPage + 4 * (u & 3) + r) * slot_elems;
+                        static_cast<unsigned>(pg) < static_cast<unsigned>(nb_ok);
+        const size_t off = (static_cast<size_t>(ok ? pg : 0) * (kContig ? 1 : kPage) + 4 * (u & 3) + r) * slot_elems;
         if (ok) vf[u].load(vbase + off); else vf[u].zero();
       }
     }
@@ -972,21 +1013,28 @@ struct KvStep {  // one 64-key step of one pool: 16 key rows x WPL words per lan
 // the hardware range check returns zeros for pages past the split, for block
 // ids outside the pool (descriptor of size 0) and for the lanes whose key is
 // past the end of the split (offset moved out of range), without branches.
-template <int WPL>
-__device__ __forceinline__ void load_step(KvStep<WPL>& dst, const unsigned char* pool,
-                                          const_i32_t* btrow, int kb, int kfin, int num_blocks,
-                                          uint32_t page_bytes, uint32_t lane_off,
+template <int WPL, bool kContig>
+__device__ __forceinline__ void load_step(KvStep<WPL>& dst, const void* pool,
+                                          const_i32_t* btrow, int row0, int kb, int kfin,
+                                          int num_blocks, uint32_t page_bytes, uint32_t lane_off,
                                           uint32_t row4_bytes, int r) {
   __amdgpu_buffer_rsrc_t rs[4];
   const int last_page = (kfin - 1) >> 4;  // block-table index of the split's last key
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) {
     const int idx = (kb >> 4) + pp;
-    const int id = btrow[min(idx, last_page)];  // scalar load, always inside the row
-    const int pg = idx <= last_page ? id : -1;
-    const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(num_blocks);
+    int pg;
+    bool ok;
+    if constexpr (kContig) {
+      pg = idx <= last_page ? row0 + idx * kPage : -1;
+      ok = pg >= 0;
+    } else {
+      const int id = btrow[min(idx, last_page)];  // scalar load, always inside the row
+      pg = idx <= last_page ? id : -1;
+      ok = static_cast<unsigned>(pg) < static_cast<unsigned>(num_blocks);
+    }
     rs[pp] = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<unsigned char*>(pool) + static_cast<size_t>(ok ? pg : 0) * page_bytes, 0,
+        page_base<kContig>(pool, ok ? pg : 0, page_bytes / kPage, page_bytes), 0,
         ok ? static_cast<int>(page_bytes) : 0, kRawBufferWord3);
   }
   const bool full = kb + 64 <= kfin;
@@ -1007,7 +1055,7 @@ __device__ __forceinline__ void load_step(KvStep<WPL>& dst, const unsigned char*
   }
 }
 
-template <int D>
+template <int D, bool kContig>
 __device__ void decode_item_bf16(const MainArgs& a, int seg, int j, int split_keys) {
   constexpr int WPL = D / 32;  // bf16 pairs per lane per key row (8 or 4 channels)
   const int lane = threadIdx.x & 63, w = wave_id();
@@ -1025,8 +1073,9 @@ __device__ void decode_item_bf16(const MainArgs& a, int seg, int j, int split_ke
   const uint32_t page_bytes = slot_bytes * kPage;
   const uint32_t lane_off = r * slot_bytes + static_cast<uint32_t>(kvh) * D * 2 + c * WPL * 4;
   const uint32_t row4_bytes = 4 * slot_bytes;
-  const unsigned char* kpool = static_cast<const unsigned char*>(a.kc);
-  const unsigned char* vpool = static_cast<const unsigned char*>(a.vc);
+  const void* kpool = a.kc;
+  const void* vpool = a.vc;
+  const int row0 = segment_row0<kContig>(a, seg);
 
   uint32_t qw[WPL];
   {
@@ -1047,8 +1096,8 @@ __device__ void decode_item_bf16(const MainArgs& a, int seg, int j, int split_ke
   for (int e = 0; e < 2 * WPL; ++e) acc[e] = 0.f;
 
   KvStep<WPL> kst, vst;
-  load_step<WPL>(kst, kpool, btrow, kbeg, kfin, a.num_blocks, page_bytes, lane_off, row4_bytes, r);
-  load_step<WPL>(vst, vpool, btrow, kbeg, kfin, a.num_blocks, page_bytes, lane_off, row4_bytes, r);
+  load_step<WPL, kContig>(kst, kpool, btrow, row0, kbeg, kfin, a.num_blocks, page_bytes, lane_off, row4_bytes, r);
+  load_step<WPL, kContig>(vst, vpool, btrow, row0, kbeg, kfin, a.num_blocks, page_bytes, lane_off, row4_bytes, r);
   for (int kb = kbeg; kb < kfin; kb += 64) {
     // partial dot products: this lane's channels of key rows 4u + r
     float pu[16];
@@ -1061,7 +1110,7 @@ __device__ void decode_item_bf16(const MainArgs& a, int seg, int j, int split_ke
     }
     // K registers are free: start the next step's K (past the split every
     // descriptor is empty and the loads return zeros without touching memory)
-    load_step<WPL>(kst, kpool, btrow, kb + 64, kfin, a.num_blocks, page_bytes, lane_off,
+    load_step<WPL, kContig>(kst, kpool, btrow, row0, kb + 64, kfin, a.num_blocks, page_bytes, lane_off,
                    row4_bytes, r);
     // reduce-scatter over the 16 lanes of the row: lane c ends with key row u = c
     {
@@ -1125,7 +1174,7 @@ __device__ void decode_item_bf16(const MainArgs& a, int seg, int j, int split_ke
         acc[2 * i + 1] = dot2_bf16(pw, pair_hi(v0, v1), acc[2 * i + 1]);
       }
     }
-    load_step<WPL>(vst, vpool, btrow, kb + 64, kfin, a.num_blocks, page_bytes, lane_off,
+    load_step<WPL, kContig>(vst, vpool, btrow, row0, kb + 64, kfin, a.num_blocks, page_bytes, lane_off,
                    row4_bytes, r);
   }
 
@@ -1169,7 +1218,7 @@ __device__ __forceinline__ int find_segment_lds(const int* prefix, int n, int x)
 
 // kSplit: this launch may meet split chunk tiles (the planner was allowed to
 // split); the instance without it keeps the unsplit roles' register allocation.
-template <typename T, int D, bool kSplit>
+template <typename T, int D, bool kSplit, bool kContig>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
   constexpr int kSmem = ChunkCfg<T>::template Sizes<D>::BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kSmem];
@@ -1303,15 +1352,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
     if (threadIdx.x == 0) s_next = claim();  // next item, claimed while this one runs
     if (kind == 1) {
       if (csplit == 1) {
-        if constexpr (sizeof(T) == 2) chunk_tile_bf16<D, false>(a, seg, p1, p2, 0, 1, smem);
-        else chunk_tile_f32<D, false>(a, seg, p1, p2, 0, 1, smem);
+        if constexpr (sizeof(T) == 2) chunk_tile_bf16<D, false, kContig>(a, seg, p1, p2, 0, 1, smem);
+        else chunk_tile_f32<D, false, kContig>(a, seg, p1, p2, 0, 1, smem);
       } else if constexpr (kSplit) {
-        if constexpr (sizeof(T) == 2) chunk_tile_bf16<D, true>(a, seg, p1, p2, p3, csplit, smem);
-        else chunk_tile_f32<D, true>(a, seg, p1, p2, p3, csplit, smem);
+        if constexpr (sizeof(T) == 2) chunk_tile_bf16<D, true, kContig>(a, seg, p1, p2, p3, csplit, smem);
+        else chunk_tile_f32<D, true, kContig>(a, seg, p1, p2, p3, csplit, smem);
       }
     } else {
-      if constexpr (sizeof(T) == 2) decode_item_bf16<D>(a, seg, p1, split_keys);
-      else decode_item<T, D>(a, seg, p1, split_keys);
+      if constexpr (sizeof(T) == 2) decode_item_bf16<D, kContig>(a, seg, p1, split_keys);
+      else decode_item<T, D, kContig>(a, seg, p1, split_keys);
     }
   }
 }
@@ -1475,18 +1524,19 @@ hipError_t side_stream(int dev, SideStream*& out) {
   return hipSuccess;
 }
 
-template <typename T, int D, bool kSplit>
+template <typename T, int D, bool kSplit, bool kContig>
 void launch_attn(const MainArgs& ma, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_kernel<T, D, kSplit>), dim3(grid), dim3(kThreads), 0, st, ma);
+  hipLaunchKernelGGL((attn_kernel<T, D, kSplit, kContig>), dim3(grid), dim3(kThreads), 0, st, ma);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool kContig>
 hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
   // Chunk tiles may be split only when even the largest number of them the
   // bounds allow (tiles_cap per head) fills at most half of split_items; every
   // other step runs the instance without the split code.
   int grid = 0;
-  hipError_t e = occupancy(info, dt, di, 0, reinterpret_cast<const void*>(attn_kernel<T, D, false>), grid);
+  hipError_t e = occupancy(info, dt, di, 0,
+                           reinterpret_cast<const void*>(attn_kernel<T, D, false, kContig>), grid);
   if (e != hipSuccess) return e;
   // For bf16, splitting pays only while it brings idle CUs into use: a second
   // item on a CU shares its MFMA and LDS with the first (measured: a bf16 chunk
@@ -1498,7 +1548,7 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
   const bool split_ok = L.ws.chunk_slots_cap >= 2 &&
                         2LL * L.ws.tiles_cap * L.num_heads <= static_cast<long long>(split_items);
   if (split_ok) {
-    e = occupancy(info, dt, di, 1, reinterpret_cast<const void*>(attn_kernel<T, D, true>), grid);
+    e = occupancy(info, dt, di, 1, reinterpret_cast<const void*>(attn_kernel<T, D, true, kContig>), grid);
     if (e != hipSuccess) return e;
   }
   SideStream* side = nullptr;
@@ -1521,6 +1571,7 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
   int32_t* tile_prefix = reinterpret_cast<int32_t*>(ws + L.ws.tile_prefix);
   int32_t* dec_prefix = reinterpret_cast<int32_t*>(ws + L.ws.dec_prefix);
   int32_t* part_prefix = reinterpret_cast<int32_t*>(ws + L.ws.part_prefix);
+  int32_t* seqlens = reinterpret_cast<int32_t*>(ws + L.ws.seqlens);
   const int head_groups = (L.num_heads + kHeadsPerDecodeItem - 1) / kHeadsPerDecodeItem;
 
   // cost of a 64-key chunk step in decode (key, head) pairs, measured roughly on
@@ -1530,17 +1581,18 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
   PlanArgs pa{L.cu_seqlens_q, L.seqlens_k, L.num_seqs, L.total_q, L.max_seqlen_q, L.max_seqlen_k,
               L.max_blocks, L.num_heads, head_groups, L.ws.parts_cap, grid * kItemsPerSlot,
               grid, L.ws.tiles_cap, split_ok ? L.ws.chunk_slots_cap : 0, chunk_first_wgs,
-              dec_first_wgs, split_items, chunk_step_cost, hdr, tile_prefix, dec_prefix,
-              part_prefix};
+              dec_first_wgs, split_items, chunk_step_cost, kContig ? L.cu_seqlens_k : nullptr,
+              L.total_k, kContig ? seqlens : nullptr, hdr, tile_prefix, dec_prefix, part_prefix};
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, L.stream, pa);
 
-  MainArgs ma{L.q, L.k_cache, L.v_cache, L.out, L.cu_seqlens_q, L.seqlens_k, L.block_table,
+  MainArgs ma{L.q, L.k_cache, L.v_cache, L.out, L.cu_seqlens_q,
+              kContig ? seqlens : L.seqlens_k, L.block_table,
               L.num_seqs, L.num_heads, L.num_kv_heads, L.num_heads / L.num_kv_heads,
               L.num_blocks, L.max_blocks, L.ws.part_stride, L.sm_scale * kLog2e, hdr,
               tile_prefix, dec_prefix, part_prefix,
               reinterpret_cast<float*>(ws + L.ws.partials),
-              reinterpret_cast<float*>(ws + L.ws.chunk_partials), 3, half};
-  auto attn = split_ok ? launch_attn<T, D, true> : launch_attn<T, D, false>;
+              reinterpret_cast<float*>(ws + L.ws.chunk_partials), L.cu_seqlens_k, 3, half};
+  auto attn = split_ok ? launch_attn<T, D, true, kContig> : launch_attn<T, D, false, kContig>;
   if (L.launch_mode == kLaunchFused) {
     attn(ma, grid, L.stream);
   } else {
@@ -1584,10 +1636,20 @@ hipError_t launch_attention(const AttnLaunch& L) {
     e = hipDeviceGetAttribute(&info.cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
   }
-  if (L.dtype == 1) {
-    return L.head_dim == 128 ? run<bf16_t, 128>(L, info, dev, 1, 1) : run<bf16_t, 64>(L, info, dev, 1, 0);
+  if (L.cu_seqlens_k) {
+    if (L.dtype == 1) {
+      return L.head_dim == 128 ? run<bf16_t, 128, true>(L, info, dev, 1, 1)
+                               : run<bf16_t, 64, true>(L, info, dev, 1, 0);
+    }
+    return L.head_dim == 128 ? run<float, 128, true>(L, info, dev, 0, 1)
+                             : run<float, 64, true>(L, info, dev, 0, 0);
   }
-  return L.head_dim == 128 ? run<float, 128>(L, info, dev, 0, 1) : run<float, 64>(L, info, dev, 0, 0);
+  if (L.dtype == 1) {
+    return L.head_dim == 128 ? run<bf16_t, 128, false>(L, info, dev, 1, 1)
+                             : run<bf16_t, 64, false>(L, info, dev, 1, 0);
+  }
+  return L.head_dim == 128 ? run<float, 128, false>(L, info, dev, 0, 1)
+                           : run<float, 64, false>(L, info, dev, 0, 0);
 }
 
 }  // namespace ha

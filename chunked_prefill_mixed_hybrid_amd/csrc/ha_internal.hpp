@@ -26,7 +26,7 @@ constexpr int kChunkSplitItems = 512;
 constexpr int kChunkSplitMinKeys = 512;
 
 // ---- workspace ---------------------------------------------------------------------
-// [header 256 B][tile_prefix (B+1)][dec_prefix (B+1)][part_prefix (B+1)]
+// [header 256 B][tile_prefix (B+1)][dec_prefix (B+1)][part_prefix (B+1)][seqlens (B+1)]
 // [partials parts_cap x H x (D + 4) fp32]
 // [chunk_partials chunk_slots_cap x H x 128 x (D + 4) fp32]; every array starts
 // on a 256-byte boundary.
@@ -56,7 +56,7 @@ static_assert(sizeof(PlanHeader) == 256, "header is 256 bytes");
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t tile_prefix, dec_prefix, part_prefix, partials, chunk_partials, total;
+  size_t tile_prefix, dec_prefix, part_prefix, seqlens, partials, chunk_partials, total;
   int parts_cap;
   int part_stride;      // floats per (part, head) or (chunk slot, head, row): m, l, 2 pad, acc[D]
   int tiles_cap;        // bound on query tiles over all chunk segments
@@ -92,6 +92,7 @@ inline WsLayout ws_layout(int num_seqs, int total_q, int max_seqlen_k, int num_h
   l.tile_prefix = off; off += arr;
   l.dec_prefix = off; off += arr;
   l.part_prefix = off; off += arr;
+  l.seqlens = off; off += arr;  // Lk per segment, derived by the planner for contiguous K/V
   l.parts_cap = parts_cap_for(num_seqs, max_seqlen_k);
   l.part_stride = head_dim + 4;
   l.partials = off;
@@ -116,8 +117,10 @@ struct AttnLaunch {
   const void* k_cache;
   const void* v_cache;
   const int32_t* cu_seqlens_q;
-  const int32_t* seqlens_k;
-  const int32_t* block_table;
+  const int32_t* seqlens_k;    // paged K/V
+  const int32_t* block_table;  // paged K/V
+  const int32_t* cu_seqlens_k; // contiguous K/V (then seqlens_k and block_table are unused)
+  int total_k;                 // contiguous K/V: rows of k and v
   void* out;
   int num_seqs, total_q, max_seqlen_q, max_seqlen_k;
   int num_heads, num_kv_heads, head_dim, num_blocks, max_blocks;

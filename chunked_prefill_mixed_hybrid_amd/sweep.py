@@ -11,10 +11,13 @@ bench workload's shape, 32 heads x 128, bf16, 16-token pages.
 
     python -m chunked_prefill_mixed_hybrid_amd.sweep [--history 1536] [--reps 50]
     python -m chunked_prefill_mixed_hybrid_amd.sweep trace
+    python -m chunked_prefill_mixed_hybrid_amd.sweep kv
 
 The first prints one JSON line per (L, decodes) point and a table; `trace`
 runs a 64-request trace through the token-budget step generator (one JSON
-line: steps, tokens/s, per-step times, fraction of the per-step rooflines).
+line: steps, tokens/s, per-step times, fraction of the per-step rooflines);
+`kv` times the attention call on paged K/V and on the same keys packed per
+segment (varlen_attn_fwd).
 Synthetic inputs (seeded), as everywhere in this package.
 """
 from __future__ import annotations
@@ -132,9 +135,59 @@ def trace(num_requests=64, budget=2048, threshold=0, prompt=(256, 4096), new_tok
     return res
 
 
+def kv_layouts(configs=(2, 5, 1), reps=30):
+    """Attention-call time on paged K/V (hybrid_attn_fwd) and on the same keys
+    packed per segment (varlen_attn_fwd), per workload config."""
+    import torch
+    from . import binding as B
+    from . import workload as W
+    res = []
+    for c in configs:
+        spec, meta = W.make_step(c)
+        ds = W.device_values(spec, meta, seed=0) if spec.dtype == W.BF16 else \
+            W.to_device(W.host_values(spec, meta, seed=0))
+        B.paged_kv_append(ds.key, ds.value, ds.slot_mapping, ds.k_cache, ds.v_cache)
+        slots = []
+        for b, lk in enumerate(meta.seqlens_k.tolist()):
+            j = np.arange(lk)
+            slots.append(meta.block_table[b, j // meta.page_size] * meta.page_size + j % meta.page_size)
+        idx = torch.from_numpy(np.concatenate(slots).astype(np.int64)).cuda()
+        nb, pg, hkv, d = ds.k_cache.shape
+        k = ds.k_cache.reshape(nb * pg, hkv, d).index_select(0, idx)
+        v = ds.v_cache.reshape(nb * pg, hkv, d).index_select(0, idx)
+        cu_k = torch.from_numpy(np.concatenate([[0], np.cumsum(meta.seqlens_k)]).astype(np.int32)).cuda()
+        out = torch.empty_like(ds.q)
+        ws = B.alloc_workspace(meta.num_seqs, meta.total_q, meta.max_seqlen_k, spec.num_heads,
+                               spec.head_dim)
+        calls = {
+            "paged": lambda: B.hybrid_attn_fwd(ds.q, ds.k_cache, ds.v_cache, ds.cu_seqlens_q,
+                                               ds.seqlens_k, ds.block_table, meta.max_seqlen_q,
+                                               meta.max_seqlen_k, out=out, workspace=ws),
+            "contiguous": lambda: B.varlen_attn_fwd(ds.q, k, v, ds.cu_seqlens_q, cu_k,
+                                                    meta.max_seqlen_q, meta.max_seqlen_k,
+                                                    out=out, workspace=ws)}
+        row = {"workload": spec.name}
+        for name, f in calls.items():
+            for _ in range(3):
+                f()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            row[name + "_us"] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+        res.append(row)
+        print(json.dumps(row), flush=True)
+        del ds, k, v, out, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("mode", nargs="?", default="tiles", choices=["tiles", "trace"])
+    ap.add_argument("mode", nargs="?", default="tiles", choices=["tiles", "trace", "kv"])
     ap.add_argument("--lengths", default=",".join(map(str, DEFAULT_LENGTHS)))
     ap.add_argument("--history", type=int, default=1536, help="chunk history H0 (keys before it)")
     ap.add_argument("--decodes", default="0,30", help="decode segments packed with the chunk")
@@ -144,6 +197,9 @@ def main(argv=None):
     B.load()  # fail loudly if the HIP library is missing
     if args.mode == "trace":
         print(json.dumps(trace()), flush=True)
+        return
+    if args.mode == "kv":
+        kv_layouts()
         return
     rows = []
     for nd in (int(x) for x in args.decodes.split(",")):

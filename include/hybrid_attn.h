@@ -170,6 +170,32 @@ ha_status hybrid_attn_fwd_two_launch(const void* q, const void* k_cache, const v
                                      void* workspace, size_t workspace_bytes,
                                      int32_t two_streams, void* stream);
 
+/*
+ * varlen_attn_fwd -- the same right-aligned causal attention over K/V packed
+ * contiguously per segment, the flash_attn_varlen_func contract the wangyu.me
+ * page describes (section on the varlen interface): segment b's keys and
+ * values are rows cu_seqlens_k[b] .. cu_seqlens_k[b+1] - 1 of k and v, so
+ * Lk_b = cu_seqlens_k[b+1] - cu_seqlens_k[b]; query rows as for
+ * hybrid_attn_fwd (right-aligned: row i sees keys 0 .. Lk_b - Lq_b + i).
+ *
+ *   k, v          device [total_k, num_kv_heads, head_dim], dtype
+ *   cu_seqlens_k  device int32 [num_seqs + 1], non-decreasing, last <= total_k
+ *   workspace     at least hybrid_attn_workspace_size(num_seqs, total_q,
+ *                 max_seqlen_k, num_heads, head_dim) bytes, 256-byte aligned
+ * Other arguments as for hybrid_attn_fwd (no block table, no page size).
+ * Segments whose key rows fall outside [0, total_k) or that break the other
+ * preconditions are skipped (rows untouched).  Same plan and arithmetic as
+ * hybrid_attn_fwd: for the same keys the outputs are byte-identical.
+ * Errors: as for hybrid_attn_fwd; HA_ERR_INVALID_ARGUMENT also for a null
+ * cu_seqlens_k or total_k < 0.
+ */
+ha_status varlen_attn_fwd(const void* q, const void* k, const void* v,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* out,
+                          int32_t num_seqs, int32_t total_q, int32_t total_k,
+                          int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_heads,
+                          int32_t num_kv_heads, int32_t head_dim, float sm_scale, ha_dtype dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

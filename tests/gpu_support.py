@@ -55,6 +55,26 @@ def plan_header(workspace) -> dict:
     return dict(zip(PLAN_HEADER_FIELDS, (int(v) for v in raw[8:8 + len(PLAN_HEADER_FIELDS)])))
 
 
+def contiguous_kv(ds: W.DeviceStep, poison_rows: int = 5):
+    """Each segment's logical keys and values gathered out of the (appended)
+    paged pools into packed [total_k, Hkv, D] buffers, followed by NaN rows, and
+    the matching cu_seqlens_k -- the same data in the varlen contiguous layout."""
+    import torch
+    m = ds.meta
+    slots = []
+    for b, lk in enumerate(m.seqlens_k.tolist()):
+        j = np.arange(lk)
+        slots.append(m.block_table[b, j // m.page_size] * m.page_size + j % m.page_size)
+    idx = torch.from_numpy(np.concatenate(slots).astype(np.int64)).to(ds.k_cache.device)
+    nb, p, hkv, d = ds.k_cache.shape
+    k = ds.k_cache.reshape(nb * p, hkv, d).index_select(0, idx)
+    v = ds.v_cache.reshape(nb * p, hkv, d).index_select(0, idx)
+    pad = torch.full((poison_rows, hkv, d), float("nan"), dtype=k.dtype, device=k.device)
+    cu_k = np.concatenate([[0], np.cumsum(m.seqlens_k)]).astype(np.int32)
+    return (torch.cat([k, pad]).contiguous(), torch.cat([v, pad]).contiguous(),
+            torch.from_numpy(cu_k).to(k.device))
+
+
 def to_f64(t) -> np.ndarray:
     return O.to_f64(W.to_host_array(t))
 

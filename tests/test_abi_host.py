@@ -87,6 +87,26 @@ def test_fwd_argument_errors(lib, entry):
         assert fwd(lib, wsb=need - 1, two_streams=1) == B.HA_ERR_WORKSPACE_TOO_SMALL
 
 
+def varlen(lib, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, cuk=FAKE, out=FAKE, B=3, T=1810, TK=10167,
+                mq=1808, mk=10000, H=2, Hkv=2, D=64, scale=0.125, dt=B.HA_DTYPE_F32, ws=FAKE,
+                wsb=1 << 30, stream=None)
+    args.update(kw)
+    return lib.varlen_attn_fwd(*args.values())
+
+
+def test_varlen_argument_errors(lib):
+    assert varlen(lib, cuk=None) == B.HA_ERR_INVALID_ARGUMENT
+    assert varlen(lib, TK=-1) == B.HA_ERR_INVALID_ARGUMENT
+    assert varlen(lib, k=None) == B.HA_ERR_INVALID_ARGUMENT
+    assert varlen(lib, Hkv=3) == B.HA_ERR_INVALID_ARGUMENT
+    assert varlen(lib, mq=20000) == B.HA_ERR_INVALID_ARGUMENT
+    assert varlen(lib, D=96) == B.HA_ERR_UNSUPPORTED
+    need = B.workspace_size(3, 1810, 10000, 2, 64)
+    assert varlen(lib, wsb=need - 1) == B.HA_ERR_WORKSPACE_TOO_SMALL
+    assert varlen(lib, T=0, wsb=need) == B.HA_OK
+
+
 def app(lib, **kw):
     args = dict(key=FAKE, value=FAKE, sm=FAKE, kc=FAKE, vc=FAKE, T=4, Hkv=2, D=128, P=16, NB=8,
                 dt=B.HA_DTYPE_BF16, stream=None)

@@ -149,6 +149,52 @@ def test_two_launch_config2_matches_fused():
     _free()
 
 
+# ---------------------------------------------------------------- contiguous K/V
+# varlen_attn_fwd over each segment's keys packed into one buffer (segments
+# start at arbitrary rows, NaN rows follow the last one): the same plan and
+# arithmetic as the paged call (chunk splits included), so the output is
+# byte-identical to it.
+CONTIG_CASES = [("sweep", 0), ("sweep", 3), ("sweep", 4), ("sweep", 6), ("sweep", 7),
+                ("sweep", 9), ("sweep", 10), ("sweep", 11), ("sweep", 12), ("sweep", 13),
+                ("split", 1)]
+
+
+@pytest.mark.parametrize("case", range(len(CONTIG_CASES)))
+def test_contiguous_kv_matches_paged(case):
+    import torch
+    kind, idx = CONTIG_CASES[case]
+    segs, hq, hkv, d, dt, seed = (SWEEP if kind == "sweep" else SPLIT_CASES)[idx]
+    spec, meta = W.custom_step(segs, hq, hkv, d, dt, seed=seed)
+    hs = W.host_values(spec, meta, seed=seed)
+    ds = _dev(hs)
+    ref, _, _ = G.oracle_full(ds, hs.k_cache, hs.v_cache)
+    G.note(f"contiguous kv {kind} case={idx} segs={segs}")
+    paged = G.gpu_step(ds)  # appends, so the pools hold every key
+    k, v, cu_k = G.contiguous_kv(ds)
+    ws = B.alloc_workspace(meta.num_seqs, meta.total_q, meta.max_seqlen_k, hq, d)
+    out = B.varlen_attn_fwd(ds.q, k, v, ds.cu_seqlens_q, cu_k, meta.max_seqlen_q, meta.max_seqlen_k,
+                            workspace=ws)
+    torch.cuda.synchronize()
+    G.compare(G.to_f64(out), ref, dt, f"contiguous {kind} {idx}")
+    assert torch.equal(out.view(torch.uint8), paged.view(torch.uint8))
+    if kind == "split":
+        assert G.plan_header(ws)["chunk_split"] > 1  # splits work on packed keys too
+
+
+def test_contiguous_kv_config2():
+    import torch
+    spec, meta = W.make_step(2)
+    ds = W.device_values(spec, meta, seed=0)
+    G.note("contiguous kv config2")
+    paged = G.gpu_step(ds)
+    k, v, cu_k = G.contiguous_kv(ds)
+    out = B.varlen_attn_fwd(ds.q, k, v, ds.cu_seqlens_q, cu_k, meta.max_seqlen_q, meta.max_seqlen_k)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.uint8), paged.view(torch.uint8))
+    del ds, k, v
+    _free()
+
+
 # ---------------------------------------------------------------- full configs
 def test_config1_worked_example():
     spec, meta = W.make_step(1)
