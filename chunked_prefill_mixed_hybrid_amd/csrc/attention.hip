@@ -80,6 +80,137 @@ __device__ __forceinline__ bool plan_segment(const PlanArgs& a, int b, int& lq, 
          lq <= a.max_q && ((lk + kPage - 1) / kPage) <= a.max_blocks;
 }
 
+// Chunk tiles are split along the keys when the longest one alone would outlast
+// an even share of the whole step's work; then every chunk tile is cut into S
+// ranges, within the item, slot and minimum-length limits.
+__device__ int chunk_split_count(const PlanArgs& a, long long csteps, long long dkeys,
+                                 long long n_ct, long long steps_max) {
+  int S = 1;
+  if (n_ct > 0 && n_ct <= a.tiles_cap && a.chunk_slots_cap >= 2) {
+    const double work = (static_cast<double>(csteps) * a.chunk_step_cost +
+                         static_cast<double>(dkeys)) * a.num_heads;
+    const double share = work / a.grid;
+    const double longest = static_cast<double>(steps_max) * a.chunk_step_cost;
+    if (longest > share) {
+      long long want = static_cast<long long>(ceil(longest / share));
+      want = min(want, static_cast<long long>(a.split_items) / (n_ct * a.num_heads));
+      want = min(want, static_cast<long long>(kChunkSplitItems) / (n_ct * a.num_heads));
+      want = min(want, static_cast<long long>(a.chunk_slots_cap) / n_ct);
+      want = min(want, steps_max * 64 / kChunkSplitMinKeys);
+      S = static_cast<int>(max(want, 1LL));
+    }
+  }
+  return S;
+}
+
+// Header fields and queue counters once the totals are known: the attention
+// kernel hands out the first item of every workgroup statically (chunk-first
+// workgroup b takes item b / 8 of chunk group b % 8, decode-first workgroup b
+// takes decode item b - chunk_first_wgs); the counters start past those items.
+__device__ void write_plan_header(const PlanArgs& a, int chunk_pairs, int dec_items, int parts,
+                                  int split, int csplit, int bad) {
+  a.tile_prefix[a.num_seqs] = chunk_pairs;
+  a.dec_prefix[a.num_seqs] = dec_items;
+  a.part_prefix[a.num_seqs] = parts;
+  a.hdr->n_chunk_tiles = chunk_pairs;
+  a.hdr->n_dec_items = dec_items;
+  a.hdr->n_parts = parts;
+  a.hdr->split = split;
+  a.hdr->chunk_split = csplit;
+  a.hdr->bad_segments = bad;
+  const int cw = a.chunk_first_wgs;
+  for (int x = 0; x < kXcdGroups; ++x) {
+    const int items = chunk_group_heads(a.num_heads, x) * chunk_pairs;
+    const int first = x < cw ? (cw - x + kXcdGroups - 1) / kXcdGroups : 0;
+    a.hdr->chunk_counter[x] = static_cast<uint32_t>(min(items, first));
+  }
+  a.hdr->dec_counter = static_cast<uint32_t>(min(dec_items, a.dec_first_wgs));
+}
+
+// Planner for steps of at most one wave of segments: lane b owns segment b;
+// every total, the split choice and the prefix sums are wave operations, with
+// no barrier.  Same results as plan_kernel.
+constexpr int kPlanSmallSegments = kWave;
+
+__global__ __launch_bounds__(kWave) void plan_kernel_small(PlanArgs a) {
+  const int b = threadIdx.x;
+  int lq = -1, lk = 0;
+  if (b < a.num_seqs) {
+    int q, k;
+    if (plan_segment(a, b, q, k)) {
+      lq = q;
+      lk = k;
+    }
+  }
+  const bool bad = b < a.num_seqs && lq < 0;
+  // decode split: the smallest candidate whose items and partial slots fit
+  int pick = kSplitCandidates - 1;
+  for (int k = 0; k < kSplitCandidates; ++k) {
+    const int sh = kSplitMinLog2 + k;
+    const long long n = lq == 1 ? (static_cast<long long>(lk) + (1LL << sh) - 1) >> sh : 0;
+    long long items = n, parts = n > 1 ? n : 0;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      items += __shfl_xor(items, m);
+      parts += __shfl_xor(parts, m);
+    }
+    if (parts <= a.parts_cap && items * a.head_groups <= static_cast<long long>(a.target_items)) {
+      pick = k;
+      break;
+    }
+  }
+  // chunk work estimate (as in plan_kernel)
+  long long csteps = 0, dkeys = lq == 1 ? lk : 0, ctiles = 0, cmax = 0;
+  if (lq >= 2) {
+    const long long nt = (lq + kChunkRows - 1) / kChunkRows;
+    const long long h0_steps = (static_cast<long long>(lk - lq) + 63) >> 6;
+    const long long last = (static_cast<long long>(lk) + 63) >> 6;
+    csteps = (nt - 1) * h0_steps + (nt - 1) * nt + last;
+    ctiles = nt;
+    cmax = last;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    csteps += __shfl_xor(csteps, m);
+    dkeys += __shfl_xor(dkeys, m);
+    ctiles += __shfl_xor(ctiles, m);
+    cmax = max(cmax, __shfl_xor(cmax, m));
+  }
+  const int csplit = chunk_split_count(a, csteps, dkeys, ctiles, cmax);
+  const int split_log = kSplitMinLog2 + pick;
+  const int split = 1 << split_log;
+  // exclusive prefix sums over the lanes
+  int v[3] = {0, 0, 0};
+  if (b < a.num_seqs) {
+    if (a.sk_out) a.sk_out[b] = lq < 0 ? 0 : lk;
+    if (lq >= 2) {
+      v[0] = (lq + kChunkRows - 1) / kChunkRows * csplit;
+    } else if (lq == 1) {
+      const int n = static_cast<int>((static_cast<unsigned>(lk) + split - 1u) >> split_log);
+      v[1] = n * a.head_groups;
+      v[2] = n > 1 ? n : 0;
+    }
+  }
+  int incl[3] = {v[0], v[1], v[2]};
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      const int o = __shfl_up(incl[c], off);
+      if (b >= off) incl[c] += o;
+    }
+  }
+  if (b < a.num_seqs) {
+    a.tile_prefix[b] = incl[0] - v[0];
+    a.dec_prefix[b] = incl[1] - v[1];
+    a.part_prefix[b] = incl[2] - v[2];
+  }
+  const int tot0 = __shfl(incl[0], kWave - 1), tot1 = __shfl(incl[1], kWave - 1);
+  const int tot2 = __shfl(incl[2], kWave - 1);
+  const int nbad = __popcll(__ballot(bad));
+  if (b == 0) write_plan_header(a, tot0, tot1, tot2, split, csplit, nbad);
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int s_lq[kPlanThreads], s_lk[kPlanThreads];  // shapes of the first segments; lq -1: skipped
   __shared__ long long s_items[32][32];
@@ -173,25 +304,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     if (tid == 0) {
       s_split_log = fit_mask ? __ffsll(static_cast<long long>(fit_mask)) - 1 : kSplitCandidates - 1;
       for (int c = 0; c < 3; ++c) s_carry[c] = 0;
-      // Chunk tiles are split along the keys when the longest one alone would
-      // outlast an even share of the whole step's work; then every chunk tile
-      // is cut into S ranges, within the item, slot and minimum-length limits.
-      int S = 1;
-      if (n_ct > 0 && n_ct <= a.tiles_cap && a.chunk_slots_cap >= 2) {
-        const double work = (static_cast<double>(csteps) * a.chunk_step_cost +
-                             static_cast<double>(dkeys)) * a.num_heads;
-        const double share = work / a.grid;
-        const double longest = static_cast<double>(steps_max) * a.chunk_step_cost;
-        if (longest > share) {
-          long long want = static_cast<long long>(ceil(longest / share));
-          want = min(want, static_cast<long long>(a.split_items) / (n_ct * a.num_heads));
-          want = min(want, static_cast<long long>(kChunkSplitItems) / (n_ct * a.num_heads));
-          want = min(want, static_cast<long long>(a.chunk_slots_cap) / n_ct);
-          want = min(want, steps_max * 64 / kChunkSplitMinKeys);
-          S = static_cast<int>(max(want, 1LL));
-        }
-      }
-      s_csplit = S;
+      s_csplit = chunk_split_count(a, csteps, dkeys, n_ct, steps_max);
     }
   }
   __syncthreads();
@@ -249,28 +362,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     if (tid < 3) s_carry[tid] += s_pass_tot[tid];
     __syncthreads();
   }
-  if (tid == 0) {
-    a.tile_prefix[a.num_seqs] = s_carry[0];
-    a.dec_prefix[a.num_seqs] = s_carry[1];
-    a.part_prefix[a.num_seqs] = s_carry[2];
-    a.hdr->n_chunk_tiles = s_carry[0];
-    a.hdr->n_dec_items = s_carry[1];
-    a.hdr->n_parts = s_carry[2];
-    a.hdr->split = split;
-    a.hdr->chunk_split = csplit;
-    a.hdr->bad_segments = s_bad;
-    // the attention kernel hands out the first item of every workgroup statically:
-    // chunk-first workgroup b takes item b / 8 of chunk group b % 8, decode-first
-    // workgroup b takes decode item b - (chunk-first workgroups of its launch);
-    // the counters start past those items
-    const int cw = a.chunk_first_wgs;
-    for (int x = 0; x < kXcdGroups; ++x) {
-      const int items = chunk_group_heads(a.num_heads, x) * s_carry[0];
-      const int first = x < cw ? (cw - x + kXcdGroups - 1) / kXcdGroups : 0;
-      a.hdr->chunk_counter[x] = static_cast<uint32_t>(min(items, first));
-    }
-    a.hdr->dec_counter = static_cast<uint32_t>(min(s_carry[1], a.dec_first_wgs));
-  }
+  if (tid == 0) write_plan_header(a, s_carry[0], s_carry[1], s_carry[2], split, csplit, s_bad);
 }
 
 // ==================================================================== attention
@@ -1583,7 +1675,10 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
               grid, L.ws.tiles_cap, split_ok ? L.ws.chunk_slots_cap : 0, chunk_first_wgs,
               dec_first_wgs, split_items, chunk_step_cost, kContig ? L.cu_seqlens_k : nullptr,
               L.total_k, kContig ? seqlens : nullptr, hdr, tile_prefix, dec_prefix, part_prefix};
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, L.stream, pa);
+  if (L.num_seqs <= kPlanSmallSegments)
+    hipLaunchKernelGGL(plan_kernel_small, dim3(1), dim3(kWave), 0, L.stream, pa);
+  else
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, L.stream, pa);
 
   MainArgs ma{L.q, L.k_cache, L.v_cache, L.out, L.cu_seqlens_q,
               kContig ? seqlens : L.seqlens_k, L.block_table,

@@ -11,7 +11,7 @@
 
 namespace ha {
 
-// One thread moves one 16-byte chunk of K and the same chunk of V.
+// Short rows: one thread moves one 16-byte chunk of K and the same chunk of V.
 // grid.x * blockDim.x >= total_tokens * chunks_per_row (checked by the launcher).
 __global__ __launch_bounds__(kThreads) void kv_append_kernel(
     const u32x4_t* __restrict__ key, const u32x4_t* __restrict__ value,
@@ -29,6 +29,26 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(
   v_cache[dst] = value[idx];
 }
 
+// Rows of at least half a workgroup of chunks (e.g. 32 heads x 128 bf16 = 512):
+// one workgroup per token, whose slot is a single scalar load, and each thread
+// moves chunks c, c + 256, ... of that row.
+__global__ __launch_bounds__(kThreads) void kv_append_rows_kernel(
+    const u32x4_t* __restrict__ key, const u32x4_t* __restrict__ value,
+    const int32_t* __restrict__ slot_mapping, u32x4_t* __restrict__ k_cache,
+    u32x4_t* __restrict__ v_cache, int chunks_per_row, long long pool_slots) {
+  const int t = blockIdx.x;
+  const int slot = __builtin_amdgcn_readfirstlane(slot_mapping[t]);
+  if (slot < 0 || slot >= pool_slots) return;  // padding token or slot outside the pool
+  const size_t src = static_cast<size_t>(t) * chunks_per_row;
+  const size_t dst = static_cast<size_t>(slot) * chunks_per_row;
+  for (int c = threadIdx.x; c < chunks_per_row; c += kThreads) {
+    const u32x4_t kv = key[src + c];
+    const u32x4_t vv = value[src + c];
+    k_cache[dst + c] = kv;
+    v_cache[dst + c] = vv;
+  }
+}
+
 hipError_t launch_kv_append(const void* key, const void* value, const int32_t* slot_mapping,
                             void* k_cache, void* v_cache, int total_tokens, int num_kv_heads,
                             int head_dim, int num_blocks, int dtype, hipStream_t stream) {
@@ -37,13 +57,21 @@ hipError_t launch_kv_append(const void* key, const void* value, const int32_t* s
   const int chunks_per_row = static_cast<int>(row_bytes / 16);  // head_dim * elem_bytes % 16 == 0
   const long long total = static_cast<long long>(total_tokens) * chunks_per_row;
   if (total == 0) return hipSuccess;
+  const long long pool_slots = static_cast<long long>(num_blocks) * kPage;
+  if (chunks_per_row >= kThreads / 2) {
+    hipLaunchKernelGGL(kv_append_rows_kernel, dim3(static_cast<unsigned>(total_tokens)),
+                       dim3(kThreads), 0, stream, static_cast<const u32x4_t*>(key),
+                       static_cast<const u32x4_t*>(value), slot_mapping,
+                       static_cast<u32x4_t*>(k_cache), static_cast<u32x4_t*>(v_cache),
+                       chunks_per_row, pool_slots);
+    return hipGetLastError();
+  }
   const long long blocks = (total + kThreads - 1) / kThreads;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kv_append_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
                      stream, static_cast<const u32x4_t*>(key), static_cast<const u32x4_t*>(value),
                      slot_mapping, static_cast<u32x4_t*>(k_cache), static_cast<u32x4_t*>(v_cache),
-                     total_tokens, chunks_per_row,
-                     static_cast<long long>(num_blocks) * kPage);
+                     total_tokens, chunks_per_row, pool_slots);
   return hipGetLastError();
 }
 
