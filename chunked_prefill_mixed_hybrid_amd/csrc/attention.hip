@@ -1395,6 +1395,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
       s_next = claim();
   }
   __syncthreads();  // LDS prefix copy complete
+  // Thread-0-only code belongs in the block at the top of this loop or right
+  // after the barriers, never between the work and the back edge: there it let
+  // the compiler split the loop so that thread 0 left the inner part through
+  // the exec mask while the other lanes went round the barriers without it (a
+  // hang; tests/test_kernel_structure.py checks the compiled loops).
   for (;;) {
     if (threadIdx.x == 0) {
       const int cur = s_next;
