@@ -1080,12 +1080,20 @@ __device__ void decode_item(const MainArgs& a, int seg, int j, int split_keys) {
 }
 
 // ---------------------------------------------------------------- decode role, bf16
-// Same lane layout as decode_item, tuned for bf16: scores with v_dot2_f32_bf16
-// on the raw bf16 pairs, the 16-lane reduce-scatter and the weight broadcast
-// on DPP row operations, P.V on bf16 pairs (weights rounded to bf16, the sum of
-// weights taken from the same rounded values), and the K / V loads of the next
-// 64-key step issued while the current one is being reduced, so every wave
-// keeps up to 32 16-byte loads in flight.
+// An item is (segment, KV split, 4 query heads).  Lane 16r + c of every wave
+// works on head 4 hg + r, channels [2 WPL c, 2 WPL c + 2 WPL), so one load
+// instruction of a wave reads the 4 heads' slices of one key row -- for
+// MHA with D = 128, 1 KB contiguous -- instead of 256-byte pieces of 4 rows:
+// on MI355X a pure read in the sliced pattern peaks near 5.4 TB/s, in 1 KB
+// pieces near 6.35 TB/s.  Wave w takes the w-th quarter of the split's keys
+// (rounded to whole 16-key steps, so every step lies in one page), keeps a
+// running (max, sum, acc) per head, and the 4 waves merge through LDS at the
+// end.  Scores with v_dot2_f32_bf16 on the
+// raw bf16 pairs and a 16-lane DPP reduce-scatter (lane c ends with key c of
+// the step); weights rounded to bf16, the sum taken from the same rounded
+// values, P.V with row_newbcast broadcasts of weight pairs; the next step's K
+// is loaded as soon as the dot products have consumed the current K, the next
+// V after P.V.
 __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
   v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
@@ -1093,54 +1101,55 @@ __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, dpp_f32<kDppQuadSwap>(v));
   return v;
 }
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<kDppRowMirror>(v);
+  v += dpp_f32<kDppRowHalfMirror>(v);
+  v += dpp_f32<kDppQuadReverse>(v);
+  v += dpp_f32<kDppQuadSwap>(v);
+  return v;
+}
 
 template <int WPL>
-struct KvStep {  // one 64-key step of one pool: 16 key rows x WPL words per lane
+struct KvStep {  // one 16-key step of one pool: 16 key rows x WPL words per lane
   uint32_t w[16][WPL];
 };
 
-// Loads one 64-key step of one pool for this lane: key rows kb + 4u + r,
-// u = 0..15, channels of lane column c.  The four pages of the step are
-// addressed through buffer descriptors (base in SGPRs, 32-bit lane offset):
-// the hardware range check returns zeros for pages past the split, for block
-// ids outside the pool (descriptor of size 0) and for the lanes whose key is
+// Loads one 16-key step (keys t0 .. t0 + 15, t0 a multiple of 16, so all in
+// one page) of one pool for this lane.  The page is addressed through a buffer
+// descriptor (base in SGPRs, 32-bit lane offset, key u at scalar offset
+// u * slot_bytes): the hardware range check returns zeros for a page past the
+// split or a block id outside the pool (descriptor of size 0) and for keys
 // past the end of the split (offset moved out of range), without branches.
 template <int WPL, bool kContig>
-__device__ __forceinline__ void load_step(KvStep<WPL>& dst, const void* pool,
-                                          const_i32_t* btrow, int row0, int kb, int kfin,
-                                          int num_blocks, uint32_t page_bytes, uint32_t lane_off,
-                                          uint32_t row4_bytes, int r) {
-  __amdgpu_buffer_rsrc_t rs[4];
-  const int last_page = (kfin - 1) >> 4;  // block-table index of the split's last key
-#pragma unroll
-  for (int pp = 0; pp < 4; ++pp) {
-    const int idx = (kb >> 4) + pp;
-    int pg;
-    bool ok;
-    if constexpr (kContig) {
-      pg = idx <= last_page ? row0 + idx * kPage : -1;
-      ok = pg >= 0;
-    } else {
-      const int id = btrow[min(idx, last_page)];  // scalar load, always inside the row
-      pg = idx <= last_page ? id : -1;
-      ok = static_cast<unsigned>(pg) < static_cast<unsigned>(num_blocks);
-    }
-    rs[pp] = __builtin_amdgcn_make_buffer_rsrc(
-        page_base<kContig>(pool, ok ? pg : 0, page_bytes / kPage, page_bytes), 0,
-        ok ? static_cast<int>(page_bytes) : 0, kRawBufferWord3);
+__device__ __forceinline__ void load_step16(KvStep<WPL>& dst, const void* pool, const_i32_t* btrow,
+                                            int row0, int t0, int kfin, int num_blocks,
+                                            uint32_t slot_bytes, uint32_t page_bytes,
+                                            uint32_t lane_off) {
+  const int idx = t0 >> 4, last_page = (kfin - 1) >> 4;
+  int pg;
+  bool ok;
+  if constexpr (kContig) {
+    pg = idx <= last_page ? row0 + idx * kPage : -1;
+    ok = pg >= 0;
+  } else {
+    const int id = btrow[min(idx, last_page)];  // scalar load, always inside the row
+    pg = idx <= last_page ? id : -1;
+    ok = static_cast<unsigned>(pg) < static_cast<unsigned>(num_blocks);
   }
-  const bool full = kb + 64 <= kfin;
-  const int lim = kfin - kb - r;  // rows 4u + r of this lane are in the split while 4u < lim
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      page_base<kContig>(pool, ok ? pg : 0, slot_bytes, page_bytes), 0,
+      ok ? static_cast<int>(page_bytes) : 0, kRawBufferWord3);
+  const int lim = kfin - t0;  // keys u < lim are in the split
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
-    const uint32_t vo = (full || 4 * u < lim) ? lane_off : kOffsetOutOfRange;
-    const uint32_t so = (u & 3) * row4_bytes;
+    const uint32_t vo = u < lim ? lane_off : kOffsetOutOfRange;
+    const uint32_t so = u * slot_bytes;
     if constexpr (WPL == 4) {
-      const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs[u >> 2], vo, so, 0));
+      const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, so, 0));
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst.w[u][i] = v[i];
     } else {
-      const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs[u >> 2], vo, so, 0));
+      const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, vo, so, 0));
       dst.w[u][0] = v[0];
       dst.w[u][1] = v[1];
     }
@@ -1148,23 +1157,25 @@ __device__ __forceinline__ void load_step(KvStep<WPL>& dst, const void* pool,
 }
 
 template <int D, bool kContig>
-__device__ void decode_item_bf16(const MainArgs& a, int seg, int j, int split_keys) {
+__device__ void decode_item_bf16(const MainArgs& a, int seg, int j, int split_keys, unsigned char* smem) {
   constexpr int WPL = D / 32;  // bf16 pairs per lane per key row (8 or 4 channels)
+  constexpr int EPL = 2 * WPL;
   const int lane = threadIdx.x & 63, w = wave_id();
   const int head_groups = (a.num_heads + kHeadsPerDecodeItem - 1) / kHeadsPerDecodeItem;
   const int split = j / head_groups, hg = j - split * head_groups;
-  const int h = hg * kHeadsPerDecodeItem + w;
-  if (h >= a.num_heads) return;
+  const int r = lane >> 4, c = lane & 15;
+  // rows past the last head (num_heads not a multiple of 4) read the group's
+  // first head and are dropped at the end
+  const int h = hg * kHeadsPerDecodeItem + r;
+  const int hq = h < a.num_heads ? h : hg * kHeadsPerDecodeItem;
   const int row = a.cu[seg], Lk = a.sk[seg];
   const int nsplit = (Lk + split_keys - 1) / split_keys;
   const int kbeg = split * split_keys, kfin = min(Lk, kbeg + split_keys);
-  const int r = lane >> 4, c = lane & 15;
-  const int kvh = h / a.group;
+  const int kvh = hq / a.group;
   const_i32_t* btrow = (const_i32_t*)(a.bt) + static_cast<size_t>(seg) * a.max_blocks;
   const uint32_t slot_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 2;
   const uint32_t page_bytes = slot_bytes * kPage;
-  const uint32_t lane_off = r * slot_bytes + static_cast<uint32_t>(kvh) * D * 2 + c * WPL * 4;
-  const uint32_t row4_bytes = 4 * slot_bytes;
+  const uint32_t lane_off = static_cast<uint32_t>(kvh) * D * 2 + c * WPL * 4;
   const void* kpool = a.kc;
   const void* vpool = a.vc;
   const int row0 = segment_row0<kContig>(a, seg);
@@ -1172,7 +1183,7 @@ __device__ void decode_item_bf16(const MainArgs& a, int seg, int j, int split_ke
   uint32_t qw[WPL];
   {
     const unsigned char* qp = static_cast<const unsigned char*>(a.q) +
-                              (static_cast<size_t>(row) * a.num_heads + h) * D * 2 + c * WPL * 4;
+                              (static_cast<size_t>(row) * a.num_heads + hq) * D * 2 + c * WPL * 4;
     if constexpr (WPL == 4) {
       const u32x4_t v = ld16(qp);
 #pragma unroll
@@ -1183,15 +1194,18 @@ __device__ void decode_item_bf16(const MainArgs& a, int seg, int j, int split_ke
       qw[1] = v[1];
     }
   }
-  float m_run = -INFINITY, l_lane = 0.f, acc[2 * WPL];
+  float m_run = -INFINITY, l_lane = 0.f, acc[EPL];
 #pragma unroll
-  for (int e = 0; e < 2 * WPL; ++e) acc[e] = 0.f;
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
 
+  const int quarter = ((kfin - kbeg + 63) >> 6) << 4;  // keys per wave, a multiple of 16
+  const int t_first = kbeg + quarter * w;
+  const int kend = min(kfin, t_first + quarter);      // this wave's keys: [t_first, kend)
   KvStep<WPL> kst, vst;
-  load_step<WPL, kContig>(kst, kpool, btrow, row0, kbeg, kfin, a.num_blocks, page_bytes, lane_off, row4_bytes, r);
-  load_step<WPL, kContig>(vst, vpool, btrow, row0, kbeg, kfin, a.num_blocks, page_bytes, lane_off, row4_bytes, r);
-  for (int kb = kbeg; kb < kfin; kb += 64) {
-    // partial dot products: this lane's channels of key rows 4u + r
+  load_step16<WPL, kContig>(kst, kpool, btrow, row0, t_first, kend, a.num_blocks, slot_bytes, page_bytes, lane_off);
+  load_step16<WPL, kContig>(vst, vpool, btrow, row0, t_first, kend, a.num_blocks, slot_bytes, page_bytes, lane_off);
+  for (int t0 = t_first; t0 < kend; t0 += 16) {
+    // partial dot products: this lane's channels of keys t0 + u
     float pu[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
@@ -1202,9 +1216,9 @@ __device__ void decode_item_bf16(const MainArgs& a, int seg, int j, int split_ke
     }
     // K registers are free: start the next step's K (past the split every
     // descriptor is empty and the loads return zeros without touching memory)
-    load_step<WPL, kContig>(kst, kpool, btrow, row0, kb + 64, kfin, a.num_blocks, page_bytes, lane_off,
-                   row4_bytes, r);
-    // reduce-scatter over the 16 lanes of the row: lane c ends with key row u = c
+    load_step16<WPL, kContig>(kst, kpool, btrow, row0, t0 + 16, kend, a.num_blocks, slot_bytes, page_bytes,
+                              lane_off);
+    // reduce-scatter over the 16 lanes of the row: lane c ends with key u = c
     {
       const bool up8 = (c & 8) != 0;
 #pragma unroll
@@ -1232,20 +1246,16 @@ __device__ void decode_item_bf16(const MainArgs& a, int seg, int j, int split_ke
       const float keep = up1 ? pu[1] : pu[0];
       pu[0] = keep + dpp_f32<kDppQuadSwap>(send);
     }
-    const int my_key = kb + 4 * c + r;
-    const float s = my_key < kfin ? pu[0] * a.scale_log2 : -INFINITY;
-    float mx = row16_max(s);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);  // finite: key kb is in range
+    const float s = t0 + c < kend ? pu[0] * a.scale_log2 : -INFINITY;
+    const float m_new = fmaxf(m_run, row16_max(s));  // finite: key t0 is in range
     const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
-    // this lane's weight rounded to bf16; pairs (key rows 2t, 2t+1) formed on even lanes
+    // this lane's weight rounded to bf16; pairs (keys 2t, 2t+1) formed on even lanes
     const uint32_t pbits = pack_bf16x2(fast_exp2(s - m_new), 0.f) & 0xffffu;
     l_lane = l_lane * alpha + __uint_as_float(pbits << 16);
     const uint32_t pair = pbits | (dpp_u32<kDppQuadSwap>(pbits) << 16);
 #pragma unroll
-    for (int e = 0; e < 2 * WPL; ++e) acc[e] *= alpha;
+    for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       uint32_t pw;
@@ -1266,32 +1276,61 @@ __device__ void decode_item_bf16(const MainArgs& a, int seg, int j, int split_ke
         acc[2 * i + 1] = dot2_bf16(pw, pair_hi(v0, v1), acc[2 * i + 1]);
       }
     }
-    load_step<WPL, kContig>(vst, vpool, btrow, row0, kb + 64, kfin, a.num_blocks, page_bytes, lane_off,
-                   row4_bytes, r);
+    load_step16<WPL, kContig>(vst, vpool, btrow, row0, t0 + 16, kend, a.num_blocks, slot_bytes, page_bytes,
+                              lane_off);
   }
 
-  const float l_tot = wave_sum(l_lane);
+  // merge the 4 waves' (max, sum, acc) of each head through LDS: wave w writes
+  // its rows, then wave w finishes head 4 hg + w over all 4 waves
+  float* s_acc = reinterpret_cast<float*>(smem);  // [wave][lane][EPL]
+  float* s_ml = s_acc + kThreads * EPL;           // [wave][row][2]
+  const float l_row = row16_sum(l_lane);
 #pragma unroll
-  for (int e = 0; e < 2 * WPL; ++e) {
-    acc[e] += __shfl_xor(acc[e], 16);
-    acc[e] += __shfl_xor(acc[e], 32);
+  for (int e = 0; e < EPL; ++e) s_acc[threadIdx.x * EPL + e] = acc[e];
+  if (c == 0) {
+    s_ml[(w * 4 + r) * 2] = m_run;
+    s_ml[(w * 4 + r) * 2 + 1] = l_row;
   }
-  if (nsplit == 1) {
-    if (r == 0) {
-      const float inv = 1.f / l_tot;
-      float o[2 * WPL];
+  __syncthreads();
+  constexpr int CPL = D / kWave;  // channels per lane in the merge
+  const int hm = hg * kHeadsPerDecodeItem + w;
+  if (hm < a.num_heads) {
+    float mw[4], mx = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 2 * WPL; ++e) o[e] = acc[e] * inv;
-      store_row<bf16_t, 2 * WPL>(static_cast<bf16_t*>(a.out) +
-                                     (static_cast<size_t>(row) * a.num_heads + h) * D + c * 2 * WPL, o);
+    for (int v = 0; v < 4; ++v) {
+      mw[v] = s_ml[(v * 4 + w) * 2];
+      mx = fmaxf(mx, mw[v]);
     }
-  } else {
-    float* pp = a.partials +
-                (static_cast<size_t>(a.part_prefix[seg] + split) * a.num_heads + h) * a.part_stride;
-    if (r == 0) store_row<float, 2 * WPL>(pp + 4 + c * 2 * WPL, acc);
-    if (lane == 0) {
-      pp[0] = m_run;
-      pp[1] = l_tot;
+    float l_tot = 0.f, o[CPL];
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) o[e] = 0.f;
+    const int ch = lane * CPL;               // first channel of this lane
+    const int src_lane = 16 * w + ch / EPL;  // lane of the compute layout holding it
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float f = mw[v] == -INFINITY ? 0.f : fast_exp2(mw[v] - mx);  // a wave with no keys adds nothing
+      l_tot = fmaf(s_ml[(v * 4 + w) * 2 + 1], f, l_tot);
+      const float* src = s_acc + (v * kWave + src_lane) * EPL + ch % EPL;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) o[e] = fmaf(src[e], f, o[e]);
+    }
+    if (nsplit == 1) {
+      const float inv = 1.f / l_tot;
+      bf16_t* op = static_cast<bf16_t*>(a.out) + (static_cast<size_t>(row) * a.num_heads + hm) * D + ch;
+      if constexpr (CPL == 2) {
+        *reinterpret_cast<uint32_t*>(op) = pack_bf16x2(o[0] * inv, o[1] * inv);
+      } else {
+        *op = static_cast<bf16_t>(pack_bf16x2(o[0] * inv, 0.f) & 0xffffu);
+      }
+    } else {
+      float* pp = a.partials +
+                  (static_cast<size_t>(a.part_prefix[seg] + split) * a.num_heads + hm) * a.part_stride;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) pp[4 + ch + e] = o[e];
+      if (lane == 0) {
+        pp[0] = mx;
+        pp[1] = l_tot;
+      }
     }
   }
 }
@@ -1456,7 +1495,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
         else chunk_tile_f32<D, true, kContig>(a, seg, p1, p2, p3, csplit, smem);
       }
     } else {
-      if constexpr (sizeof(T) == 2) decode_item_bf16<D, kContig>(a, seg, p1, split_keys);
+      if constexpr (sizeof(T) == 2) decode_item_bf16<D, kContig>(a, seg, p1, split_keys, smem);
       else decode_item<T, D, kContig>(a, seg, p1, split_keys);
     }
   }

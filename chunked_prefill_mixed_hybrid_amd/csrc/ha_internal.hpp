@@ -17,7 +17,7 @@ constexpr int kSplitMin = 1 << kSplitMinLog2;  // smallest decode KV split, in k
 constexpr int kSplitCandidates = 23;  // decode split sizes kSplitMin << k, k < 23 (up to 2^30)
 constexpr int kPartsMax = 16384;    // cap on (segment, split) partial slots
 constexpr int kItemsPerSlot = 16;   // decode work items aimed at per resident workgroup
-constexpr int kHeadsPerDecodeItem = 4;  // one head per wave
+constexpr int kHeadsPerDecodeItem = 4;  // bf16: one head per 16-lane row of every wave; fp32: one per wave
 constexpr int kMaxSeqlenK = 1 << 30;
 // Chunk tiles are split along the keys only when a few long tiles would
 // otherwise outlast the rest of the step: at most this many (tile, head, split)
