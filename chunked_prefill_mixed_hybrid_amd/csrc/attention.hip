@@ -1120,6 +1120,10 @@ struct KvStep {  // one 16-key step of one pool: 16 key rows x WPL words per lan
 // u * slot_bytes): the hardware range check returns zeros for a page past the
 // split or a block id outside the pool (descriptor of size 0) and for keys
 // past the end of the split (offset moved out of range), without branches.
+// The loads are non-temporal: each decode key is read once per item, and on
+// MI355X streaming it through L2 with normal priority evicted the chunk
+// tiles' shared K/V (a step of 2 chunks of 512 and 30 decodes: 246.7 -> 225.2 us
+// with the hint).
 template <int WPL, bool kContig>
 __device__ __forceinline__ void load_step16(KvStep<WPL>& dst, const void* pool, const_i32_t* btrow,
                                             int row0, int t0, int kfin, int num_blocks,
@@ -1145,11 +1149,11 @@ __device__ __forceinline__ void load_step16(KvStep<WPL>& dst, const void* pool, 
     const uint32_t vo = u < lim ? lane_off : kOffsetOutOfRange;
     const uint32_t so = u * slot_bytes;
     if constexpr (WPL == 4) {
-      const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, so, 0));
+      const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, so, kLoadNonTemporal));
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst.w[u][i] = v[i];
     } else {
-      const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, vo, so, 0));
+      const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, vo, so, kLoadNonTemporal));
       dst.w[u][0] = v[0];
       dst.w[u][1] = v[1];
     }

@@ -85,6 +85,10 @@ template <> struct Elem<bf16_t> {
 constexpr int kRawBufferWord3 = 0x00020000;
 // A buffer offset past every descriptor's range: loads return 0.
 constexpr uint32_t kOffsetOutOfRange = 0x80000000u;
+// Cache-policy operand of a buffer load: nt (non-temporal) on gfx950 -- the
+// lines are marked for early eviction, so a stream read once does not push
+// reused data (chunk tiles' K/V shared through L2, partials) out of the caches.
+constexpr int kLoadNonTemporal = 2;
 
 // ---- 16-byte global / LDS accesses ------------------------------------------------
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
