@@ -50,6 +50,10 @@ SWEEP = [
     # chunk lengths one past a tile multiple, as in the tile-quantisation sweep
     ([(1025, 2561), (1, 3000), (1, 700)], 8, 8, 128, W.BF16, 13),
     ([(1153, 1153), (1, 64)], 4, 4, 128, W.BF16, 14),
+    # bf16 decode rows of heads past the last one (6 heads: the second group of
+    # 4 has 2), GQA groups of 2 and of 8
+    ([(1, 1), (1, 40), (1, 700), (1, 257), (20, 90)], 6, 3, 128, W.BF16, 15),
+    ([(1, 3000), (1, 65), (1, 16), (40, 40)], 16, 2, 64, W.BF16, 16),
 ]
 
 
@@ -156,7 +160,7 @@ def test_two_launch_config2_matches_fused():
 # byte-identical to it.
 CONTIG_CASES = [("sweep", 0), ("sweep", 3), ("sweep", 4), ("sweep", 6), ("sweep", 7),
                 ("sweep", 9), ("sweep", 10), ("sweep", 11), ("sweep", 12), ("sweep", 13),
-                ("split", 1)]
+                ("sweep", 14), ("sweep", 15), ("split", 1)]
 
 
 @pytest.mark.parametrize("case", range(len(CONTIG_CASES)))
