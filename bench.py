@@ -168,6 +168,7 @@ def main():
     torch.cuda.synchronize()
     attn_ms = np.array([e1.elapsed_time(e2) for _, e1, e2 in ev])
     append_ms = np.array([e0.elapsed_time(e1) for e0, e1, _ in ev])
+    step_ms = np.array([e0.elapsed_time(e2) for e0, _, e2 in ev])
 
     # cold steps: a 1 GiB write before each step evicts L2 and the 256 MB MALL
     cold = []
@@ -230,11 +231,18 @@ def main():
         "append_us": round(float(np.mean(append_ms)) * 1e3, 2),
         "attn_us": round(attn_us, 2),
         "cold_us_per_step": round(float(np.median(cold)) * 1e3, 2) if cold else None,
+        "step_us_percentiles": percentiles(step_ms),
+        "cold_us_percentiles": percentiles(np.array(cold)) if cold else None,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(ds, spec, meta)
     print(json.dumps(result), flush=True)
+
+
+def percentiles(ms):
+    """p10 / p50 / p90 of per-step durations given in ms, in us."""
+    return {f"p{q}": round(float(np.percentile(ms, q)) * 1e3, 2) for q in (10, 50, 90)}
 
 
 if __name__ == "__main__":
