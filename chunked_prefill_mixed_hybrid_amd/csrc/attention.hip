@@ -25,11 +25,14 @@
 //         tiles of 64 keys staged in LDS; S^T = K Q^T and O^T += V^T P^T on
 //         32x32 MFMA (bf16 inputs, fp32 accumulate); the mask is evaluated only
 //         on tiles that cross the causal diagonal.
-//       - decode role: 4 waves = 4 heads of one (segment, KV split); each wave
-//         streams its head's rows of 64 keys per step with 16-byte loads,
-//         reduces the 16-lane partial dot products with a butterfly
-//         reduce-scatter, and keeps fp32 (m, l, acc) per lane.  Splits of a
-//         segment write partial (m, l, acc) rows that combine_kernel merges.
+//       - decode role (bf16): 4 heads of one (segment, KV split); each 16-lane
+//         row of a wave owns one head, so a 16-byte load instruction reads one
+//         key row of the 4 heads, and the 4 waves take a quarter of the keys
+//         each, streamed 16 keys per step with non-temporal loads; 16-lane
+//         butterfly reduce-scatter of the partial dot products, fp32 (m, l, acc)
+//         per lane, merged across the waves through LDS.  (fp32: one head per
+//         wave.)  Splits of a segment write partial (m, l, acc) rows that
+//         combine_kernel merges.
 #include <mutex>
 
 #include "ha_common.hpp"
