@@ -17,7 +17,7 @@ HA_OK, HA_ERR_INVALID_ARGUMENT, HA_ERR_UNSUPPORTED, HA_ERR_WORKSPACE_TOO_SMALL, 
 HA_DTYPE_F32, HA_DTYPE_BF16 = 0, 1
 
 EXPORTED = ("ha_status_string", "paged_kv_append", "hybrid_attn_workspace_size", "hybrid_attn_fwd",
-            "hybrid_attn_fwd_two_launch", "varlen_attn_fwd")
+            "hybrid_attn_fwd_two_launch", "varlen_attn_fwd", "hybrid_step_fwd")
 
 
 class HybridAttnError(RuntimeError):
@@ -59,6 +59,9 @@ def load(path: Path | str | None = None) -> ctypes.CDLL:
     lib.varlen_attn_fwd.argtypes = ([vp, vp, vp, i32p, i32p, vp] + [i32] * 8 +
                                     [ctypes.c_float, ctypes.c_int, vp, ctypes.c_size_t, vp])
     lib.varlen_attn_fwd.restype = ctypes.c_int
+    lib.hybrid_step_fwd.argtypes = ([vp, vp, i32p, vp, vp, vp, i32p, i32p, i32p, vp] + [i32] * 10 +
+                                    [ctypes.c_float, ctypes.c_int, vp, ctypes.c_size_t, vp])
+    lib.hybrid_step_fwd.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -141,6 +144,40 @@ def hybrid_attn_fwd_two_launch(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, blo
     return _attn("hybrid_attn_fwd_two_launch", q, k_cache, v_cache, cu_seqlens_q, seqlens_k,
                  block_table, max_seqlen_q, max_seqlen_k, out, sm_scale, workspace, stream,
                  (1 if two_streams else 0,))
+
+
+def hybrid_step_fwd(key, value, slot_mapping, q, k_cache, v_cache, cu_seqlens_q, seqlens_k,
+                    block_table, max_seqlen_q, max_seqlen_k, out=None, sm_scale=None,
+                    workspace=None, stream=None):
+    """One whole mixed step: paged_kv_append(key, value, slot_mapping) into the
+    pools, then hybrid_attn_fwd -- the same result, with the append and the
+    planner sharing a launch when the step allows it."""
+    import torch
+    t, hq, d = q.shape
+    nb, p, hkv, d2 = k_cache.shape
+    if d2 != d or v_cache.shape != k_cache.shape or key.shape != (t, hkv, d) or value.shape != key.shape:
+        raise ValueError("hybrid_step_fwd: shape mismatch")
+    b = seqlens_k.shape[0]
+    if (cu_seqlens_q.shape != (b + 1,) or block_table.dim() != 2 or block_table.shape[0] != b
+            or slot_mapping.shape != (t,)):
+        raise ValueError("hybrid_step_fwd: metadata shapes")
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = alloc_workspace(b, t, max_seqlen_k, hq, d, device=q.device)
+    scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(d)
+    dt = q.dtype
+    st = load().hybrid_step_fwd(
+        _dev(key, "key", dt), _dev(value, "value", dt),
+        _dev(slot_mapping, "slot_mapping", torch.int32), _dev(q, "q", dt),
+        _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(seqlens_k, "seqlens_k", torch.int32),
+        _dev(block_table, "block_table", torch.int32), _dev(out, "out", dt),
+        b, t, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, p, nb, block_table.shape[1],
+        scale, _dtype_code(q), _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(stream))
+    _check("hybrid_step_fwd", st)
+    return out
 
 
 def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, out=None,

@@ -64,7 +64,9 @@ ha_status attention_launch(const void* q, const void* k_cache, const void* v_cac
                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                            int32_t page_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                            float sm_scale, ha_dtype dtype, void* workspace,
-                           size_t workspace_bytes, void* stream, int launch_mode) {
+                           size_t workspace_bytes, void* stream, int launch_mode,
+                           const void* append_key = nullptr, const void* append_value = nullptr,
+                           const int32_t* slot_mapping = nullptr) {
   if (num_seqs < 1 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_heads < 1 ||
       num_kv_heads < 1 || head_dim < 1 || page_size < 1 || num_blocks < 1 ||
       max_blocks_per_seq < 1)
@@ -107,6 +109,9 @@ ha_status attention_launch(const void* q, const void* k_cache, const void* v_cac
   L.workspace = static_cast<unsigned char*>(workspace);
   L.ws = ws;
   L.stream = static_cast<hipStream_t>(stream);
+  L.append_key = append_key;
+  L.append_value = append_value;
+  L.slot_mapping = slot_mapping;
   return ha::launch_attention(L) == hipSuccess ? HA_OK : HA_ERR_HIP;
 }
 
@@ -126,6 +131,23 @@ ha_status hybrid_attn_fwd(const void* q, const void* k_cache, const void* v_cach
                           out, num_seqs, total_q, max_seqlen_q, max_seqlen_k, num_heads,
                           num_kv_heads, head_dim, page_size, num_blocks, max_blocks_per_seq,
                           sm_scale, dtype, workspace, workspace_bytes, stream, ha::kLaunchFused);
+}
+
+ha_status hybrid_step_fwd(const void* key, const void* value, const int32_t* slot_mapping,
+                          const void* q, void* k_cache, void* v_cache,
+                          const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                          const int32_t* block_table, void* out, int32_t num_seqs,
+                          int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t page_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                          float sm_scale, ha_dtype dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (total_q > 0 && (!key || !value || !slot_mapping)) return HA_ERR_INVALID_ARGUMENT;
+  return attention_launch(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table, nullptr, 0,
+                          out, num_seqs, total_q, max_seqlen_q, max_seqlen_k, num_heads,
+                          num_kv_heads, head_dim, page_size, num_blocks, max_blocks_per_seq,
+                          sm_scale, dtype, workspace, workspace_bytes, stream, ha::kLaunchFused,
+                          key, value, slot_mapping);
 }
 
 ha_status hybrid_attn_fwd_two_launch(const void* q, const void* k_cache, const void* v_cache,

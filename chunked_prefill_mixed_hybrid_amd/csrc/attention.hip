@@ -135,8 +135,8 @@ __device__ void write_plan_header(const PlanArgs& a, int chunk_pairs, int dec_it
 // no barrier.  Same results as plan_kernel.
 constexpr int kPlanSmallSegments = kWave;
 
-__global__ __launch_bounds__(kWave) void plan_kernel_small(PlanArgs a) {
-  const int b = threadIdx.x;
+__device__ __forceinline__ void plan_small(const PlanArgs& a) {  // the 64 lanes of one wave
+  const int b = threadIdx.x & (kWave - 1);
   int lq = -1, lk = 0;
   if (b < a.num_seqs) {
     int q, k;
@@ -212,6 +212,21 @@ __global__ __launch_bounds__(kWave) void plan_kernel_small(PlanArgs a) {
   const int tot2 = __shfl(incl[2], kWave - 1);
   const int nbad = __popcll(__ballot(bad));
   if (b == 0) write_plan_header(a, tot0, tot1, tot2, split, csplit, nbad);
+}
+
+__global__ __launch_bounds__(kWave) void plan_kernel_small(PlanArgs a) { plan_small(a); }
+
+// A step's append and the small planner in one launch (hybrid_step_fwd):
+// workgroup 0 plans with its first wave while workgroups 1 .. T copy the new
+// token rows into the pools, so the planner's latency hides behind the copy
+// instead of running as a launch of its own between the append and the
+// attention.  The planner reads only metadata, none of the pools.
+__global__ __launch_bounds__(kThreads) void append_plan_kernel(PlanArgs pa, AppendRows rows) {
+  if (blockIdx.x == 0) {
+    if (threadIdx.x < kWave) plan_small(pa);
+    return;
+  }
+  append_row(rows, static_cast<int>(blockIdx.x) - 1);
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
@@ -1726,10 +1741,29 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
               grid, L.ws.tiles_cap, split_ok ? L.ws.chunk_slots_cap : 0, chunk_first_wgs,
               dec_first_wgs, split_items, chunk_step_cost, kContig ? L.cu_seqlens_k : nullptr,
               L.total_k, kContig ? seqlens : nullptr, hdr, tile_prefix, dec_prefix, part_prefix};
-  if (L.num_seqs <= kPlanSmallSegments)
+  // hybrid_step_fwd: the append first -- with the small planner in the same
+  // launch when the rows are wide (one workgroup per token), else on its own
+  const long long chunks_per_row = static_cast<long long>(L.num_kv_heads) * L.head_dim * sizeof(T) / 16;
+  const bool fused_append = L.append_key && L.num_seqs <= kPlanSmallSegments &&
+                            chunks_per_row >= kThreads / 2;
+  if (L.append_key && !fused_append) {
+    e = launch_kv_append(L.append_key, L.append_value, L.slot_mapping, const_cast<void*>(L.k_cache),
+                         const_cast<void*>(L.v_cache), L.total_q, L.num_kv_heads, L.head_dim,
+                         L.num_blocks, sizeof(T) == 4 ? 0 : 1, L.stream);
+    if (e != hipSuccess) return e;
+  }
+  if (fused_append) {
+    const AppendRows rows{static_cast<const uint4*>(L.append_key), static_cast<const uint4*>(L.append_value),
+                          L.slot_mapping, static_cast<uint4*>(const_cast<void*>(L.k_cache)),
+                          static_cast<uint4*>(const_cast<void*>(L.v_cache)),
+                          static_cast<int>(chunks_per_row), static_cast<long long>(L.num_blocks) * kPage};
+    hipLaunchKernelGGL(append_plan_kernel, dim3(static_cast<unsigned>(L.total_q) + 1), dim3(kThreads), 0,
+                       L.stream, pa, rows);
+  } else if (L.num_seqs <= kPlanSmallSegments) {
     hipLaunchKernelGGL(plan_kernel_small, dim3(1), dim3(kWave), 0, L.stream, pa);
-  else
+  } else {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, L.stream, pa);
+  }
 
   MainArgs ma{L.q, L.k_cache, L.v_cache, L.out, L.cu_seqlens_q,
               kContig ? seqlens : L.seqlens_k, L.block_table,

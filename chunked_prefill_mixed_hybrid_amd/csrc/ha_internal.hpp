@@ -130,7 +130,38 @@ struct AttnLaunch {
   unsigned char* workspace;
   WsLayout ws;
   hipStream_t stream;
+  // hybrid_step_fwd: this step's new keys and values go into the pools first
+  // (key / value [total_q, Hkv, D], slot_mapping [total_q]); null for the
+  // attention-only entry points
+  const void* append_key = nullptr;
+  const void* append_value = nullptr;
+  const int32_t* slot_mapping = nullptr;
 };
+
+// One token row of the append: the row's K and V (chunks_per_row 16-byte
+// chunks each) go to slot slot_mapping[t]; a padding token (slot < 0) or a
+// slot outside the pool is skipped.  Called by one workgroup per token.
+struct AppendRows {
+  const uint4* key;
+  const uint4* value;
+  const int32_t* slot_mapping;
+  uint4* k_cache;
+  uint4* v_cache;
+  int chunks_per_row;
+  long long pool_slots;
+};
+__device__ __forceinline__ void append_row(const AppendRows& a, int t) {
+  const int slot = __builtin_amdgcn_readfirstlane(a.slot_mapping[t]);
+  if (slot < 0 || slot >= a.pool_slots) return;
+  const size_t src = static_cast<size_t>(t) * a.chunks_per_row;
+  const size_t dst = static_cast<size_t>(slot) * a.chunks_per_row;
+  for (int c = threadIdx.x; c < a.chunks_per_row; c += kThreads) {
+    const uint4 kv = a.key[src + c];
+    const uint4 vv = a.value[src + c];
+    a.k_cache[dst + c] = kv;
+    a.v_cache[dst + c] = vv;
+  }
+}
 
 hipError_t launch_kv_append(const void* key, const void* value, const int32_t* slot_mapping,
                             void* k_cache, void* v_cache, int total_tokens, int num_kv_heads,

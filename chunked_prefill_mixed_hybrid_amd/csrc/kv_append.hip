@@ -32,21 +32,8 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(
 // Rows of at least half a workgroup of chunks (e.g. 32 heads x 128 bf16 = 512):
 // one workgroup per token, whose slot is a single scalar load, and each thread
 // moves chunks c, c + 256, ... of that row.
-__global__ __launch_bounds__(kThreads) void kv_append_rows_kernel(
-    const u32x4_t* __restrict__ key, const u32x4_t* __restrict__ value,
-    const int32_t* __restrict__ slot_mapping, u32x4_t* __restrict__ k_cache,
-    u32x4_t* __restrict__ v_cache, int chunks_per_row, long long pool_slots) {
-  const int t = blockIdx.x;
-  const int slot = __builtin_amdgcn_readfirstlane(slot_mapping[t]);
-  if (slot < 0 || slot >= pool_slots) return;  // padding token or slot outside the pool
-  const size_t src = static_cast<size_t>(t) * chunks_per_row;
-  const size_t dst = static_cast<size_t>(slot) * chunks_per_row;
-  for (int c = threadIdx.x; c < chunks_per_row; c += kThreads) {
-    const u32x4_t kv = key[src + c];
-    const u32x4_t vv = value[src + c];
-    k_cache[dst + c] = kv;
-    v_cache[dst + c] = vv;
-  }
+__global__ __launch_bounds__(kThreads) void kv_append_rows_kernel(AppendRows a) {
+  append_row(a, blockIdx.x);
 }
 
 hipError_t launch_kv_append(const void* key, const void* value, const int32_t* slot_mapping,
@@ -59,11 +46,11 @@ hipError_t launch_kv_append(const void* key, const void* value, const int32_t* s
   if (total == 0) return hipSuccess;
   const long long pool_slots = static_cast<long long>(num_blocks) * kPage;
   if (chunks_per_row >= kThreads / 2) {
+    const AppendRows rows{static_cast<const uint4*>(key), static_cast<const uint4*>(value),
+                          slot_mapping, static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache),
+                          chunks_per_row, pool_slots};
     hipLaunchKernelGGL(kv_append_rows_kernel, dim3(static_cast<unsigned>(total_tokens)),
-                       dim3(kThreads), 0, stream, static_cast<const u32x4_t*>(key),
-                       static_cast<const u32x4_t*>(value), slot_mapping,
-                       static_cast<u32x4_t*>(k_cache), static_cast<u32x4_t*>(v_cache),
-                       chunks_per_row, pool_slots);
+                       dim3(kThreads), 0, stream, rows);
     return hipGetLastError();
   }
   const long long blocks = (total + kThreads - 1) / kThreads;

@@ -143,6 +143,38 @@ ha_status hybrid_attn_fwd(const void* q, const void* k_cache, const void* v_cach
                           size_t workspace_bytes, void* stream);
 
 /*
+ * hybrid_step_fwd -- one whole mixed step: paged_kv_append of this step's new
+ * keys and values, then hybrid_attn_fwd, in the order the wangyu.me page
+ * gives for vLLM (section "输入组装": the new K/V are written through
+ * slot_mapping before the varlen paged attention reads the history).
+ *
+ * key, value    [total_q, num_kv_heads, head_dim], dtype -- the new tokens are
+ *               this step's query rows, in the same packed order
+ * slot_mapping  [total_q] int32, device: slot page * 16 + offset of each new
+ *               token (negative: padding, skipped)
+ * q, k_cache, v_cache, metadata, out, workspace: as for hybrid_attn_fwd; the
+ * pools are written (the appended slots) and then read.
+ *
+ * Result: byte for byte what paged_kv_append followed by hybrid_attn_fwd on
+ * the same stream produce (pools and out).  For steps of at most 64 segments
+ * whose K/V rows are at least 128 16-byte chunks (num_kv_heads * head_dim *
+ * element size >= 2 KB), the append and the planner share one launch, which
+ * saves the planner's own launch; otherwise the kernels of the two calls run
+ * in sequence.  Errors: those of both calls (HA_ERR_INVALID_ARGUMENT also for
+ * null key, value or slot_mapping when total_q > 0); nothing is launched on
+ * an error.
+ */
+ha_status hybrid_step_fwd(const void* key, const void* value, const int32_t* slot_mapping,
+                          const void* q, void* k_cache, void* v_cache,
+                          const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                          const int32_t* block_table, void* out, int32_t num_seqs,
+                          int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t page_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                          float sm_scale, ha_dtype dtype, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * hybrid_attn_fwd_two_launch -- the same computation as hybrid_attn_fwd, but
  * with the chunk (prefill) role and the decode role in two separate kernel
  * launches instead of one fused launch: the "separate prefill and decode

@@ -87,6 +87,28 @@ def test_fwd_argument_errors(lib, entry):
         assert fwd(lib, wsb=need - 1, two_streams=1) == B.HA_ERR_WORKSPACE_TOO_SMALL
 
 
+def step(lib, **kw):
+    args = dict(key=FAKE, value=FAKE, sm=FAKE, q=FAKE, kc=FAKE, vc=FAKE, cu=FAKE, sk=FAKE, bt=FAKE,
+                out=FAKE, B=3, T=1810, mq=1808, mk=10000, H=2, Hkv=2, D=64, P=16, NB=644, MB=625,
+                scale=0.125, dt=B.HA_DTYPE_F32, ws=FAKE, wsb=1 << 30, stream=None)
+    args.update(kw)
+    return lib.hybrid_step_fwd(*args.values())
+
+
+def test_step_argument_errors(lib):
+    assert step(lib, key=None) == B.HA_ERR_INVALID_ARGUMENT
+    assert step(lib, value=None) == B.HA_ERR_INVALID_ARGUMENT
+    assert step(lib, sm=None) == B.HA_ERR_INVALID_ARGUMENT
+    assert step(lib, Hkv=3) == B.HA_ERR_INVALID_ARGUMENT
+    assert step(lib, q=None) == B.HA_ERR_INVALID_ARGUMENT
+    assert step(lib, ws=ctypes.c_void_p(0x100010)) == B.HA_ERR_INVALID_ARGUMENT
+    assert step(lib, D=96) == B.HA_ERR_UNSUPPORTED
+    need = B.workspace_size(3, 1810, 10000, 2, 64)
+    assert step(lib, wsb=need - 1) == B.HA_ERR_WORKSPACE_TOO_SMALL
+    # no new tokens: nothing to append or attend, nothing enqueued
+    assert step(lib, T=0, key=None, value=None, sm=None, wsb=need) == B.HA_OK
+
+
 def varlen(lib, **kw):
     args = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, cuk=FAKE, out=FAKE, B=3, T=1810, TK=10167,
                 mq=1808, mk=10000, H=2, Hkv=2, D=64, scale=0.125, dt=B.HA_DTYPE_F32, ws=FAKE,

@@ -199,6 +199,70 @@ def test_contiguous_kv_config2():
     _free()
 
 
+# ---------------------------------------------------------------- whole-step entry point
+# hybrid_step_fwd = paged_kv_append then hybrid_attn_fwd; the append and the
+# small planner share a launch for wide rows (Hkv*D*e >= 2 KB) and <= 64
+# segments, the calls run one after the other otherwise.  Pools and output
+# must be byte-identical to the two calls, and the output within the oracle's
+# tolerance.
+STEP_CASES = [("sweep", 10), ("sweep", 12), ("sweep", 0), ("sweep", 4), ("many", 0)]
+
+
+def _step_case(kind, idx):
+    if kind == "sweep":
+        return SWEEP[idx]
+    # more than one wave of segments: the block-wide planner, separate launches
+    segs = [(1, 17 + 37 * i) for i in range(70)] + [(130, 400)]
+    return segs, 8, 8, 128, W.BF16, 31
+
+
+def _step(ds, ws):
+    import torch
+    m = ds.meta
+    out = torch.empty_like(ds.q)
+    B.hybrid_step_fwd(ds.key, ds.value, ds.slot_mapping, ds.q, ds.k_cache, ds.v_cache,
+                      ds.cu_seqlens_q, ds.seqlens_k, ds.block_table, m.max_seqlen_q,
+                      m.max_seqlen_k, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("case", STEP_CASES)
+def test_step_entry_matches_two_calls(case):
+    import torch
+    segs, hq, hkv, d, dt, seed = _step_case(*case)
+    spec, meta = W.custom_step(segs, hq, hkv, d, dt, seed=seed)
+    hs = W.host_values(spec, meta, seed=seed)
+    G.note(f"step entry case={case} segs={len(segs)} H={hq}/{hkv} D={d} {dt}")
+    ds_a, ds_b = _dev(hs), _dev(hs)
+    ref, kc_ref, vc_ref = G.oracle_full(ds_a, hs.k_cache, hs.v_cache)
+    ws = B.alloc_workspace(meta.num_seqs, meta.total_q, meta.max_seqlen_k, hq, d)
+    out_a = G.gpu_step(ds_a, workspace=ws)
+    out_b = _step(ds_b, ws)
+    assert (out_b.view(torch.uint8).cpu().numpy().tobytes() ==
+            out_a.view(torch.uint8).cpu().numpy().tobytes())
+    kc, vc = G.host_pools(ds_b)
+    assert kc.tobytes() == kc_ref.tobytes() and vc.tobytes() == vc_ref.tobytes()
+    G.compare(G.to_f64(out_b), ref, dt, f"step entry {case}")
+
+
+def test_step_entry_config2():
+    spec, meta = W.make_step(2)
+    ds = W.device_values(spec, meta, seed=0)
+    kc0, vc0 = G.host_pools(ds)
+    ref, kc_ref, vc_ref = G.oracle_full(ds, kc0, vc0)
+    del kc0, vc0
+    G.note("step entry config2 bf16 H=32 D=128 (append and planner in one launch)")
+    ws = B.alloc_workspace(meta.num_seqs, meta.total_q, meta.max_seqlen_k, spec.num_heads,
+                           spec.head_dim)
+    out = _step(ds, ws)
+    kc, vc = G.host_pools(ds)
+    assert kc.tobytes() == kc_ref.tobytes() and vc.tobytes() == vc_ref.tobytes()
+    G.compare(G.to_f64(out), ref, W.BF16, "step entry config 2")
+    del ds
+    _free()
+
+
 # ---------------------------------------------------------------- full configs
 def test_config1_worked_example():
     spec, meta = W.make_step(1)
