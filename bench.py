@@ -2,13 +2,15 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
 
-A step is paged_kv_append followed by hybrid_attn_fwd over one synthetic batch
-already resident in HBM.  Default workload: 2 prefill chunks of 512 (histories
-0 and 1536) + 30 decodes with history U[512, 4096], 32 heads x 128, bf16,
-16-token pages, shuffled block ids.  Prints ONE JSON line: microseconds per
-step, the fraction of the step roofline max(FLOPs / MFMA peak, bytes / HBM
-peak), a roofline object for the attention call (HIP events on the stream it
-runs on) and the CPU oracle's time on the host cores as a baseline.
+A step is the append of the new tokens' K/V followed by the attention over one
+synthetic batch already resident in HBM: one hybrid_step_fwd call (default), or
+paged_kv_append then hybrid_attn_fwd (--entry calls).  Default workload: 2
+prefill chunks of 512 (histories 0 and 1536) + 30 decodes with history
+U[512, 4096], 32 heads x 128, bf16, 16-token pages, shuffled block ids.  Prints
+ONE JSON line: microseconds per step, the fraction of the step roofline
+max(FLOPs / MFMA peak, bytes / HBM peak), a roofline object for the timed call
+(HIP events on the stream it runs on) and the CPU oracle's time on the host
+cores as a baseline.
 """
 from __future__ import annotations
 
@@ -49,14 +51,16 @@ def algorithmic_work(meta, spec):
             "step_bytes": kv_bytes + qo_bytes + append_bytes + meta_bytes}
 
 
-def profiled_traffic(workload_name):
-    """HBM bytes per attn_kernel launch from the committed rocprofv3 counter
-    summary of this workload, or None when there is none or the kernel sources
-    changed since the counters were taken."""
+def profiled_traffic(workload_name, unit):
+    """HBM bytes per timed call (unit "step": hybrid_step_fwd; "attn": the
+    attention call) from the committed rocprofv3 counter summary of this
+    workload, or None when there is none or the kernel sources changed since
+    the counters were taken."""
     import hashlib
     from pathlib import Path
     root = Path(__file__).resolve().parent
-    prof = root / "profiles" / f"attn_kernel_{workload_name.replace('mixed_', 'mixed_')}.txt"
+    name = f"step_{workload_name}" if unit == "step" else f"attn_kernel_{workload_name}"
+    prof = root / "profiles" / f"{name}.txt"
     if not prof.exists():
         return None
     fields = dict(line.split(": ", 1) for line in prof.read_text().splitlines()
@@ -102,6 +106,9 @@ def main():
                     help="extra steps each preceded by a 1 GiB cache-flush write")
     ap.add_argument("--launch", default="fused", choices=["fused", "serial", "two-streams"],
                     help="fused: hybrid_attn_fwd; serial / two-streams: the two-launch baseline")
+    ap.add_argument("--entry", default="step", choices=["step", "calls"],
+                    help="step: one hybrid_step_fwd call per step; calls: paged_kv_append, then "
+                         "the attention call")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -135,7 +142,14 @@ def main():
                                          meta.max_seqlen_k, out=out, workspace=ws,
                                          two_streams=args.launch == "two-streams", stream=stream)
 
+    one_call = args.entry == "step" and args.launch == "fused"
+
     def step():
+        if one_call:
+            B.hybrid_step_fwd(ds.key, ds.value, ds.slot_mapping, ds.q, ds.k_cache, ds.v_cache,
+                              ds.cu_seqlens_q, ds.seqlens_k, ds.block_table, meta.max_seqlen_q,
+                              meta.max_seqlen_k, out=out, workspace=ws, stream=stream)
+            return
         B.paged_kv_append(ds.key, ds.value, ds.slot_mapping, ds.k_cache, ds.v_cache, stream=stream)
         attention()
 
@@ -156,7 +170,17 @@ def main():
     wall = time.perf_counter() - t0
     gpu_ms = t_start.elapsed_time(t_end)
 
-    # per-call durations (HIP events on the stream the kernels run on), a second pass
+    # the timed call on its own (HIP events on the stream the kernels run on)
+    call_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    for e0, e1 in call_ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    call_ms = np.array([e0.elapsed_time(e1) for e0, e1 in call_ev])
+
+    # the append and the attention call separately (reference), a further pass
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for e0, e1, e2 in ev:
@@ -197,20 +221,30 @@ def main():
     t_hbm_us = w["step_bytes"] / (PEAK_HBM_GBS * 1e9) * 1e6
     roof_us = max(t_mfma_us, t_hbm_us)
     attn_us = float(np.mean(attn_ms)) * 1e3
-    attn_bound = "hbm" if w["attn_bytes"] / (PEAK_HBM_GBS * 1e9) >= w["flops"] / (peak_tf * 1e12) else "mfma"
+    # the roofline unit: the whole step call (append + attention) with the step's
+    # bytes, or the attention call with its own bytes when the two are separate
+    unit_us = float(np.mean(call_ms)) * 1e3 if one_call else attn_us
+    unit_bytes = w["step_bytes"] if one_call else w["attn_bytes"]
+    attn_bound = "hbm" if unit_bytes / (PEAK_HBM_GBS * 1e9) >= w["flops"] / (peak_tf * 1e12) else "mfma"
     if attn_bound == "hbm":
-        achieved = w["attn_bytes"] / (attn_us * 1e-6) / 1e9
+        achieved = unit_bytes / (unit_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
     else:
-        achieved = w["flops"] / (attn_us * 1e-6) / 1e12
+        achieved = w["flops"] / (unit_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_tf,
                 "unit": "TFLOP/s", "frac": round(achieved / peak_tf, 4), "traffic": None}
-    roof["kernel"] = ("hybrid_attn_fwd (plan_kernel + attn_kernel + combine_kernel, back to back)"
-                      if args.launch == "fused" else
-                      f"hybrid_attn_fwd_two_launch ({args.launch}: plan, chunk launch, decode launch, combine)")
-    roof["avg_us"] = round(attn_us, 2)
-    roof["traffic"] = profiled_traffic(spec.name) if args.launch == "fused" else None
+    if one_call:
+        roof["kernel"] = ("hybrid_step_fwd (append + planner in one launch, attn_kernel, combine_kernel, "
+                          "back to back)")
+    elif args.launch == "fused":
+        roof["kernel"] = "hybrid_attn_fwd (plan_kernel + attn_kernel + combine_kernel, back to back)"
+    else:
+        roof["kernel"] = (f"hybrid_attn_fwd_two_launch ({args.launch}: plan, chunk launch, decode launch, "
+                          "combine)")
+    roof["avg_us"] = round(unit_us, 2)
+    roof["traffic"] = profiled_traffic(spec.name, "step" if one_call else "attn") \
+        if args.launch == "fused" else None
 
     result = {
         "metric": METRIC, "value": round(us_step, 2), "unit": "us/step", "n_gpus": 1,
@@ -221,7 +255,8 @@ def main():
                    "num_heads": spec.num_heads, "num_kv_heads": spec.num_kv_heads,
                    "head_dim": spec.head_dim, "page_size": meta.page_size,
                    "max_seqlen_q": meta.max_seqlen_q, "max_seqlen_k": meta.max_seqlen_k,
-                   "seed": args.seed, "launch": args.launch},
+                   "seed": args.seed, "launch": args.launch,
+                   "entry": "hybrid_step_fwd" if one_call else "paged_kv_append + attention"},
         "gpu_us_per_step": round(1e3 * gpu_ms / args.steps, 2),
         "tflops": round(w["flops"] / (us_step * 1e-6) / 1e12, 2),
         "kv_gbps": round(w["kv_bytes"] / (us_step * 1e-6) / 1e9, 1),
@@ -231,7 +266,7 @@ def main():
         "append_us": round(float(np.mean(append_ms)) * 1e3, 2),
         "attn_us": round(attn_us, 2),
         "cold_us_per_step": round(float(np.median(cold)) * 1e3, 2) if cold else None,
-        "step_us_percentiles": percentiles(step_ms),
+        "step_us_percentiles": percentiles(call_ms if one_call else step_ms),
         "cold_us_percentiles": percentiles(np.array(cold)) if cold else None,
         "roofline": roof,
     }
