@@ -1533,42 +1533,69 @@ __device__ void merge_chunk_tiles(const MainArgs& a, int blk) {
   const int S = a.hdr->chunk_split;
   if (S <= 1) return;
   constexpr int QPR = 4, CPT = D / QPR, NV = CPT / 4;
+  constexpr int RPB = kThreads / QPR;       // rows of a tile merged by one workgroup pass
+  constexpr int GROUPS = kChunkRows / RPB;  // row groups per (tile, head)
+  constexpr int BATCH = 4;                  // key ranges whose partials are loaded together
   const int n_pairs = a.hdr->n_chunk_tiles / S * a.num_heads;
   const size_t sstep = static_cast<size_t>(a.num_heads) * kChunkRows * a.part_stride;
   const int c0 = (threadIdx.x % QPR) * CPT;
-  for (int p = blk; p < n_pairs; p += kChunkMergeBlocks) {
+  for (int u = blk; u < n_pairs * GROUPS; u += kChunkMergeBlocks) {
+    const int p = u / GROUPS, grp = u - p * GROUPS;
     const int ti = p / a.num_heads, h = p - ti * a.num_heads;  // tile over all chunk segments
     const int seg = find_segment(a.tile_prefix, a.num_seqs, ti * S);
     const int tile = ti - a.tile_prefix[seg] / S;
     const int q0 = a.cu[seg], Lq = a.cu[seg + 1] - q0;
     const size_t slot0 = static_cast<size_t>(a.tile_prefix[seg] + tile * S);
-    for (int rr = threadIdx.x / QPR; rr < kChunkRows; rr += kThreads / QPR) {
-      const int row = tile * kChunkRows + rr;
-      if (row >= Lq) break;
-      const float* base = a.chunk_partials + ((slot0 * a.num_heads + h) * kChunkRows + rr) * a.part_stride;
-      float mx = -INFINITY;  // finite: range 0 holds key 0, which every row sees
-      for (int sp = 0; sp < S; ++sp) mx = fmaxf(mx, base[sp * sstep]);
-      float l = 0.f;
-      f32x4_t o[NV];
+    const int rr = grp * RPB + static_cast<int>(threadIdx.x) / QPR;
+    const int row = tile * kChunkRows + rr;
+    if (row >= Lq) continue;
+    const float* base = a.chunk_partials + ((slot0 * a.num_heads + h) * kChunkRows + rr) * a.part_stride;
+    // one online pass over the ranges, BATCH at a time: the loads of a batch are
+    // independent, so a row waits for S / BATCH round trips instead of 2 S; an
+    // empty range (max -inf) weighs 0, and range 0 holds key 0, which every row
+    // sees, so the running max is finite after the first batch
+    float mx = -INFINITY, l = 0.f;
+    f32x4_t o[NV];
 #pragma unroll
-      for (int i = 0; i < NV; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      for (int sp = 0; sp < S; ++sp) {
-        const float* pp = base + sp * sstep;
-        const float wgt = fast_exp2(pp[0] - mx);
-        l = fmaf(pp[1], wgt, l);
+    for (int i = 0; i < NV; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += BATCH) {
+      float mv[BATCH], lv[BATCH];
+      f32x4_t ov[BATCH][NV];
 #pragma unroll
-        for (int i = 0; i < NV; ++i) o[i] += wgt * *reinterpret_cast<const f32x4_t*>(pp + 4 + c0 + 4 * i);
+      for (int j = 0; j < BATCH; ++j) {
+        const bool in = s0 + j < S;
+        const float* pp = base + static_cast<size_t>(in ? s0 + j : 0) * sstep;
+        mv[j] = in ? pp[0] : -INFINITY;
+        lv[j] = in ? pp[1] : 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+          ov[j][i] = in ? *reinterpret_cast<const f32x4_t*>(pp + 4 + c0 + 4 * i) : f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
-      const float inv = 1.f / l;
-      T* op = static_cast<T*>(a.out) + (static_cast<size_t>(q0 + row) * a.num_heads + h) * D + c0;
+      float bm = mx;
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const f32x4_t v = o[i] * inv;
-        if constexpr (sizeof(T) == 2) {
-          st8(op + 4 * i, u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
-        } else {
-          *reinterpret_cast<f32x4_t*>(op + 4 * i) = v;
-        }
+      for (int j = 0; j < BATCH; ++j) bm = fmaxf(bm, mv[j]);
+      const float sc = mx == -INFINITY ? 0.f : fast_exp2(mx - bm);
+      l *= sc;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) o[i] *= sc;
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        const float wgt = mv[j] == -INFINITY ? 0.f : fast_exp2(mv[j] - bm);
+        l = fmaf(lv[j], wgt, l);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) o[i] += wgt * ov[j][i];
+      }
+      mx = bm;
+    }
+    const float inv = 1.f / l;
+    T* op = static_cast<T*>(a.out) + (static_cast<size_t>(q0 + row) * a.num_heads + h) * D + c0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const f32x4_t v = o[i] * inv;
+      if constexpr (sizeof(T) == 2) {
+        st8(op + 4 * i, u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
+      } else {
+        *reinterpret_cast<f32x4_t*>(op + 4 * i) = v;
       }
     }
   }
