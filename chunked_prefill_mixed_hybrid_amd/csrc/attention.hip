@@ -471,11 +471,17 @@ template <> struct ChunkCfg<bf16_t> {
 };
 template <> struct ChunkCfg<float> {
   template <int D> struct Sizes {
-    static constexpr int BN = D == 128 ? 32 : 64;
-    static constexpr int ROWF = D + 4;  // floats per key row (K and V)
-    static constexpr int BYTES = 2 * BN * ROWF * 4;
+    static constexpr int BN = D == 128 ? 32 : 64;  // 4 keys x 4 channels staged per thread
+    static constexpr int ROWF = D + 4;             // floats per key row of the K tile
+    static constexpr int STAGE = (BN * ROWF + D * BN) * 4;  // K natural + V^T
+    static constexpr int BYTES = 2 * STAGE;        // double buffered
   };
 };
+// 16-byte chunk swizzle of row d of the fp32 V^T tile (rows of NCH chunks of 4
+// keys): the transposed writes (rows 4c + i, c over the lanes) and the MFMA
+// operand reads (consecutive rows) both land on distinct bank groups.
+template <int NCH>
+__device__ __forceinline__ int vt_swz_f32(int d) { return (d ^ (d >> 2)) & (NCH - 1); }
 
 // ---------------------------------------------------------------- chunk KV splits
 // Keys [kb0, kb1) of split `split` out of `nsplit` of a chunk tile whose keys
@@ -761,6 +767,12 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, int
 }
 
 // ---------------------------------------------------------------- chunk role, fp32
+// Same tile and online softmax as the bf16 role on v_mfma_f32_32x32x2f32.  The
+// contraction of S^T = K Q^T pairs channel s (half-wave 0) with channel D/2 + s
+// (half-wave 1) in MFMA step s, so a lane's K and Q operands are D/2
+// consecutive floats, read 4 at a time.  V is staged transposed (V^T[d][key],
+// swizzled 16-byte chunks of 4 keys) so that the P.V operand of 8 consecutive
+// keys is two 16-byte reads.  Two LDS stages, one barrier per key step.
 template <int D, bool kSplit, bool kContig>
 __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, int split, int nsplit,
                                unsigned char* smem) {
@@ -770,11 +782,11 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, int 
   }
   using Cfg = ChunkCfg<float>::Sizes<D>;
   constexpr int BN = Cfg::BN, NKB = BN / 32, KS = D / 2, NM = D / 32, ROWF = Cfg::ROWF;
-  constexpr int CPR = D / 4;
-  constexpr int LOADS = BN * CPR / kThreads;
-  static_assert(LOADS * kThreads == BN * CPR, "tile load must divide evenly");
-  float* Ks = reinterpret_cast<float*>(smem);
-  float* Vs = Ks + BN * ROWF;
+  constexpr int STAGE = Cfg::STAGE;
+  constexpr int CPR = D / 4;   // 16-byte chunks per key row
+  constexpr int NCH = BN / 4;  // 16-byte chunks per V^T row
+  static_assert(BN * CPR == 4 * kThreads, "each thread stages 4 keys x 4 channels of a tile");
+  static_assert((kWave / CPR) * 4 <= kPage, "a wave's tile loads stay inside one page");
 
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int qc = lane & 31, g = lane >> 5;
@@ -790,114 +802,150 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, int 
   const bool wave_active = wrow0 < rows_end;
   const int pi = key_perm(qc);
 
-  float qf[KS];  // lane supplies Q[my_row][2s + g]
+  float qf[KS];  // lane supplies Q[my_row][g * KS + s]
   {
     const bool ok = my_row < Lq;
     const float* qp = static_cast<const float*>(a.q) +
-                      (static_cast<size_t>(q0 + (ok ? my_row : 0)) * a.num_heads + h) * D + g;
+                      (static_cast<size_t>(q0 + (ok ? my_row : 0)) * a.num_heads + h) * D + g * KS;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = ok ? qp[2 * s] : 0.f;
+    for (int s = 0; s < KS; s += 4) {
+      const f32x4_t v = ok ? *reinterpret_cast<const f32x4_t*>(qp + s) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qf[s + e] = v[e];
+    }
   }
   f32x16_t acc[NM];
 #pragma unroll
   for (int m = 0; m < NM; ++m) acc[m] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Tile loads as in the bf16 role: load `it` of every thread reads one page,
-  // uniform per wave, through a buffer descriptor; keys at or past kb1 read 0.
+  // Tile loads: thread (j4, c4) reads channels [4 c4, 4 c4 + 4) of keys
+  // 4 j4 .. 4 j4 + 3; a wave's keys lie in one page, so the page id is one
+  // scalar block-table read and the gathers are buffer loads; keys at or past
+  // kb1 read 0 (offset out of range, or an empty descriptor past the pages).
   const_i32_t* btrow = (const_i32_t*)(a.bt) + static_cast<size_t>(seg) * a.max_blocks;
   const int last_page = (max(kb1, 1) - 1) >> 4;
   const uint32_t slot_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 4;
   const uint32_t page_bytes = slot_bytes * kPage;
   const uint32_t head_off = static_cast<uint32_t>(kvh) * D * 4;
   const int krow0 = segment_row0<kContig>(a, seg);  // first key row (contiguous K/V)
-  u32x4_t kreg[LOADS], vreg[LOADS];
-  auto page_rsrc = [&](const void* pool, int k0, int pidx) {
-    const int id = segment_page<kContig>(btrow, krow0, (k0 >> 4) + pidx, last_page, a.num_blocks);
-    return __builtin_amdgcn_make_buffer_rsrc(page_base<kContig>(pool, id, slot_bytes, page_bytes), 0,
-                                             id >= 0 ? static_cast<int>(page_bytes) : 0,
-                                             kRawBufferWord3);
-  };
+  const int c4 = tid % CPR, j4 = tid / CPR;
+  const int pidx = (w * kWave / CPR) * 4 / kPage;  // page of this wave's keys within a tile
+  u32x4_t kreg[4], vreg[4];
   auto issue_tile = [&](int k0) {
+    const int id = segment_page<kContig>(btrow, krow0, (k0 >> 4) + pidx, last_page, a.num_blocks);
+    const int range = id >= 0 ? static_cast<int>(page_bytes) : 0;
+    const auto kr = __builtin_amdgcn_make_buffer_rsrc(page_base<kContig>(a.kc, id, slot_bytes, page_bytes),
+                                                      0, range, kRawBufferWord3);
+    const auto vr = __builtin_amdgcn_make_buffer_rsrc(page_base<kContig>(a.vc, id, slot_bytes, page_bytes),
+                                                      0, range, kRawBufferWord3);
 #pragma unroll
-    for (int it = 0; it < LOADS; ++it) {
-      const int key = (it * kThreads + tid) / CPR;
-      const int pidx = (it * kThreads + w * kWave) / (16 * CPR);  // uniform per wave
-      const uint32_t off = (k0 + key < kb1)
-                               ? (key & 15) * slot_bytes + head_off + (tid % CPR) * 16
-                               : kOffsetOutOfRange;
-      const auto kr = page_rsrc(a.kc, k0, pidx);
-      const auto vr = page_rsrc(a.vc, k0, pidx);
+    for (int it = 0; it < 4; ++it) {
+      const int key = 4 * j4 + it;
+      const uint32_t off = (k0 + key < kb1) ? (key & 15) * slot_bytes + head_off + c4 * 16
+                                            : kOffsetOutOfRange;
       kreg[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
       vreg[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0));
     }
   };
-
-  if (kb0 < kb1) issue_tile(kb0);
-  for (int k0 = kb0; k0 < kb1; k0 += BN) {
-    __syncthreads();
+  // registers -> one LDS stage: K natural Ks[key][d], V transposed Vt[d][key]
+  // (the 4 x 4 block transposed in registers, one 16-byte write per channel)
+  auto store_tile = [&](unsigned char* st) {
+    float* Ks = reinterpret_cast<float*>(st);
+    float* Vt = Ks + BN * ROWF;
 #pragma unroll
-    for (int it = 0; it < LOADS; ++it) {
-      const int idx = it * kThreads + tid;
-      st16(Ks + (idx / CPR) * ROWF + (idx % CPR) * 4, kreg[it]);
-      st16(Vs + (idx / CPR) * ROWF + (idx % CPR) * 4, vreg[it]);
+    for (int it = 0; it < 4; ++it) st16(Ks + (4 * j4 + it) * ROWF + 4 * c4, kreg[it]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 4 * c4 + i;
+      st16(Vt + d * BN + 4 * (j4 ^ vt_swz_f32<NCH>(d)),
+           u32x4_t{vreg[0][i], vreg[1][i], vreg[2][i], vreg[3][i]});
     }
-    __syncthreads();
-    issue_tile(k0 + BN);
-    if (!wave_active || k0 > H0 + wrow0 + 31) continue;
-    const bool need_mask = (k0 + BN - 1) > (H0 + wrow0);
+  };
 
-    f32x16_t sacc[NKB];
+  if (kb0 < kb1) {
+    issue_tile(kb0);
+    store_tile(smem);
+    issue_tile(kb0 + BN);
+    __syncthreads();
+  }
+  for (int k0 = kb0, i = 0; k0 < kb1; k0 += BN, ++i) {
+    const float* Ks = reinterpret_cast<const float*>(smem + (i & 1) * STAGE);
+    const float* Vt = Ks + BN * ROWF;
+    if (wave_active && k0 <= H0 + wrow0 + 31) {  // else the tile is invisible to this wave
+      const bool need_mask = (k0 + BN - 1) > (H0 + wrow0);
+      f32x16_t sacc[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      sacc[kb] = f32x16_t{};
-      const float* kr = Ks + (kb * 32 + pi) * ROWF + g;
+      for (int kb = 0; kb < NKB; ++kb) {
+        sacc[kb] = f32x16_t{};
+        const float* kr = Ks + (kb * 32 + pi) * ROWF + g * KS;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) sacc[kb] = mfma_f32(kr[2 * s], qf[s], sacc[kb]);
-    }
-    float tmax = -INFINITY;
+        for (int s = 0; s < KS; s += 4) {
+          const f32x4_t kf = *reinterpret_cast<const f32x4_t*>(kr + s);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float x = sacc[kb][v] * a.scale_log2;
-        if (need_mask) {
-          const int kp = k0 + kb * 32 + ((v >> 3) << 4) + (g << 3) + (v & 7);
-          if (kp > H0 + my_row) x = -INFINITY;
+          for (int e = 0; e < 4; ++e) sacc[kb] = mfma_f32(kf[e], qf[s + e], sacc[kb]);
         }
-        sacc[kb][v] = x;
-        tmax = fmaxf(tmax, x);
       }
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = fast_exp2(sacc[kb][v] - m_use);
-        sacc[kb][v] = p;
-        psum += p;
-      }
-    }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int m = 0; m < NM; ++m) acc[m] *= alpha;
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
+      float tmax = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-        for (int n = 0; n < 16; ++n) {
-          const int key = kb * 32 + ((n >> 3) << 4) + (g << 3) + (n & 7);
-          acc[m] = mfma_f32(Vs[key * ROWF + m * 32 + qc], sacc[kb][n], acc[m]);
+        for (int v = 0; v < 16; ++v) {
+          float x = sacc[kb][v] * a.scale_log2;
+          if (need_mask) {
+            const int kp = k0 + kb * 32 + ((v >> 3) << 4) + (g << 3) + (v & 7);
+            if (kp > H0 + my_row) x = -INFINITY;
+          }
+          sacc[kb][v] = x;
+          tmax = fmaxf(tmax, x);
+        }
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m_run, tmax);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = fast_exp2(sacc[kb][v] - m_use);
+          sacc[kb][v] = p;
+          psum += p;
+        }
+      }
+      l_run = l_run * alpha + psum;
+      if (__any(alpha != 1.f)) {  // no row max moved: the accumulators need no rescale
+#pragma unroll
+        for (int m = 0; m < NM; ++m) acc[m] *= alpha;
+      }
+      // O^T += V^T P^T: value n of sacc[kb] is key kb*32 + 16 (n/8) + 8 g + n % 8,
+      // i.e. 16-byte V^T chunk kb*8 + 4 (n/8) + 2 g + (n % 8) / 4
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            const int d = m * 32 + qc;
+            const float* vrow = Vt + d * BN;
+            const int ch = kb * 8 + 4 * u + 2 * g, sw = vt_swz_f32<NCH>(d);
+            const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(vrow + 4 * (ch ^ sw));
+            const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(vrow + 4 * ((ch + 1) ^ sw));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[m] = mfma_f32(v0[e], sacc[kb][8 * u + e], acc[m]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[m] = mfma_f32(v1[e], sacc[kb][8 * u + 4 + e], acc[m]);
+          }
         }
       }
     }
+    if (k0 + BN < kb1) {
+      store_tile(smem + ((i + 1) & 1) * STAGE);  // tile i+1, loaded during tile i
+      issue_tile(k0 + 2 * BN);                   // tile i+2 streams in
+    }
+    __syncthreads();
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);  // lanes l and l^32 share a row
@@ -924,6 +972,8 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, int 
 // Work item codes of the persistent kernel: chunk item i of group x is
 // x << 24 | i, decode item d is kDecodeTag | d.
 constexpr int kDecodeTag = 1 << 28, kDone = 0x7fffffff;
+// scheduler state: the next item is to be claimed at the top of the item loop
+constexpr int kPending = 0x7ffffffe;
 
 // ---------------------------------------------------------------- decode role
 // One wave = one head of one (segment, KV split).  Lane l = 16 r + c covers
@@ -1401,7 +1451,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
   // so both roles run side by side on every CU.  A launch for one role only
   // (roles) never opens the other kind's queues.  The first item of every workgroup is assigned statically (the planner
   // starts the counters past those items); afterwards the next item is claimed
-  // with an atomic at the start of the current one, hiding the claim's latency.
+  // with an atomic at the start of the current one, hiding the claim's latency
+  // (fp32 chunk items: at their end).
   const int half = a.chunk_wgs;
   const bool chunk_first = static_cast<int>(blockIdx.x) < half;
   const int my_group = blockIdx.x % kXcdGroups;
@@ -1418,16 +1469,41 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
 #pragma unroll
     for (int x = 0; x < kXcdGroups; ++x)
       if (seen[x] >= static_cast<unsigned>(chunk_group_heads(a.num_heads, x) * n_tiles)) open &= ~(1u << x);
-    for (int k = 0; k < kXcdGroups && open; ++k) {
-      const int x = (my_group + k) % kXcdGroups;
-      if (!(open & (1u << x))) continue;
-      const int n = chunk_group_heads(a.num_heads, x) * n_tiles;
-      const int c = static_cast<int>(atomicAdd(&a.hdr->chunk_counter[x], 1u));
-      if (c < n) {
-        s_chunk_open = open;
-        return (x << 24) | c;
+    if constexpr (sizeof(T) == 4) {
+      // fp32 steps have few heads, so most groups are empty and most
+      // workgroups claim from another group: after its own group, a workgroup
+      // tries the open groups starting at an offset that differs between the
+      // workgroups of a group, which spreads the atomics over every open
+      // counter instead of queueing them on the first.  (Kept out of the bf16
+      // instances, where the extra state costs register spills.)  Each pass
+      // closes one group: at most kXcdGroups passes.
+      while (open) {
+        int x = my_group;
+        if (!(open & (1u << my_group))) {
+          unsigned m = open;
+          for (int j = (static_cast<int>(blockIdx.x) / kXcdGroups) % __popc(open); j > 0; --j) m &= m - 1;
+          x = __ffs(m) - 1;
+        }
+        const int n = chunk_group_heads(a.num_heads, x) * n_tiles;
+        const int c = static_cast<int>(atomicAdd(&a.hdr->chunk_counter[x], 1u));
+        if (c < n) {
+          s_chunk_open = open;
+          return (x << 24) | c;
+        }
+        open &= ~(1u << x);
       }
-      open &= ~(1u << x);
+    } else {
+      for (int k = 0; k < kXcdGroups && open; ++k) {
+        const int x = (my_group + k) % kXcdGroups;
+        if (!(open & (1u << x))) continue;
+        const int n = chunk_group_heads(a.num_heads, x) * n_tiles;
+        const int c = static_cast<int>(atomicAdd(&a.hdr->chunk_counter[x], 1u));
+        if (c < n) {
+          s_chunk_open = open;
+          return (x << 24) | c;
+        }
+        open &= ~(1u << x);
+      }
     }
     s_chunk_open = open;
     return kDone;
@@ -1463,6 +1539,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
   // hang; tests/test_kernel_structure.py checks the compiled loops).
   for (;;) {
     if (threadIdx.x == 0) {
+      if (sizeof(T) == 4 && s_next == kPending) s_next = claim();  // claim deferred by a chunk item
       const int cur = s_next;
       int kind = 0, seg = 0, p1 = 0, p2 = 0, p3 = 0;  // kind: 0 done, 1 chunk, 2 decode
       if (cur != kDone && (cur & kDecodeTag)) {
@@ -1507,7 +1584,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
     const int p3 = __builtin_amdgcn_readfirstlane(s_work[4]);
     __syncthreads();
     if (kind == 0) break;
-    if (threadIdx.x == 0) s_next = claim();  // next item, claimed while this one runs
+    // the next item, claimed while this one runs (hides the atomic's latency).
+    // fp32 chunk items are claimed only once done: in the fp32 worked-example
+    // shape there are about as many items as workgroups, and an item reserved
+    // at the start of a long chunk tile waits behind it while other workgroups
+    // run dry.  (bf16 instances keep the early claim: the deferred one costs
+    // them register spills.)
+    if (threadIdx.x == 0) s_next = (sizeof(T) == 4 && kind == 1) ? kPending : claim();
     if (kind == 1) {
       if (csplit == 1) {
         if constexpr (sizeof(T) == 2) chunk_tile_bf16<D, false, kContig>(a, seg, p1, p2, 0, 1, smem);
