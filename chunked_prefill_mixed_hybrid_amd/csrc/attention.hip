@@ -62,6 +62,7 @@ struct PlanArgs {
   int32_t* tile_prefix;
   int32_t* dec_prefix;
   int32_t* part_prefix;
+  int chunk_gsub;  // queue groups per head (chunk_group_items)
 };
 
 constexpr int kPlanThreads = 1024;
@@ -120,10 +121,11 @@ __device__ void write_plan_header(const PlanArgs& a, int chunk_pairs, int dec_it
   a.hdr->n_parts = parts;
   a.hdr->split = split;
   a.hdr->chunk_split = csplit;
+  a.hdr->chunk_gsub = a.chunk_gsub;
   a.hdr->bad_segments = bad;
   const int cw = a.chunk_first_wgs;
   for (int x = 0; x < kXcdGroups; ++x) {
-    const int items = chunk_group_heads(a.num_heads, x) * chunk_pairs;
+    const int items = chunk_group_items(a.num_heads, a.chunk_gsub, chunk_pairs, x);
     const int first = x < cw ? (cw - x + kXcdGroups - 1) / kXcdGroups : 0;
     a.hdr->chunk_counter[x] = static_cast<uint32_t>(min(items, first));
   }
@@ -217,16 +219,21 @@ __device__ __forceinline__ void plan_small(const PlanArgs& a) {  // the 64 lanes
 __global__ __launch_bounds__(kWave) void plan_kernel_small(PlanArgs a) { plan_small(a); }
 
 // A step's append and the small planner in one launch (hybrid_step_fwd):
-// workgroup 0 plans with its first wave while workgroups 1 .. T copy the new
-// token rows into the pools, so the planner's latency hides behind the copy
-// instead of running as a launch of its own between the append and the
-// attention.  The planner reads only metadata, none of the pools.
+// workgroup 0 plans with its first wave while the other workgroups copy the
+// new token rows into the pools (one workgroup per token for rows of at least
+// half a workgroup of 16-byte chunks, else one thread per chunk), so the
+// planner's latency hides behind the copy instead of running as a launch of
+// its own between the append and the attention.  The planner reads only
+// metadata, none of the pools.
 __global__ __launch_bounds__(kThreads) void append_plan_kernel(PlanArgs pa, AppendRows rows) {
   if (blockIdx.x == 0) {
     if (threadIdx.x < kWave) plan_small(pa);
     return;
   }
-  append_row(rows, static_cast<int>(blockIdx.x) - 1);
+  if (rows.chunks_per_row >= kThreads / 2)
+    append_row(rows, static_cast<int>(blockIdx.x) - 1);
+  else
+    append_chunk(rows, static_cast<long long>(blockIdx.x - 1) * kThreads + threadIdx.x);
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
@@ -1436,6 +1443,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
   const int n_dec = a.hdr->n_dec_items;
   const int split_keys = a.hdr->split;
   const int csplit = kSplit ? a.hdr->chunk_split : 1;
+  const int gsub = sizeof(T) == 4 ? a.hdr->chunk_gsub : 1;  // bf16 planners always write 1
   const bool lds_lookup = a.num_seqs <= kLdsSegments;
   if (lds_lookup) {
     for (int i = threadIdx.x; i <= a.num_seqs; i += kThreads) {
@@ -1468,7 +1476,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
     unsigned open = s_chunk_open;
 #pragma unroll
     for (int x = 0; x < kXcdGroups; ++x)
-      if (seen[x] >= static_cast<unsigned>(chunk_group_heads(a.num_heads, x) * n_tiles)) open &= ~(1u << x);
+      if (seen[x] >= static_cast<unsigned>(chunk_group_items(a.num_heads, gsub, n_tiles, x))) open &= ~(1u << x);
     if constexpr (sizeof(T) == 4) {
       // fp32 steps have few heads, so most groups are empty and most
       // workgroups claim from another group: after its own group, a workgroup
@@ -1484,7 +1492,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
           for (int j = (static_cast<int>(blockIdx.x) / kXcdGroups) % __popc(open); j > 0; --j) m &= m - 1;
           x = __ffs(m) - 1;
         }
-        const int n = chunk_group_heads(a.num_heads, x) * n_tiles;
+        const int n = chunk_group_items(a.num_heads, gsub, n_tiles, x);
         const int c = static_cast<int>(atomicAdd(&a.hdr->chunk_counter[x], 1u));
         if (c < n) {
           s_chunk_open = open;
@@ -1496,7 +1504,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
       for (int k = 0; k < kXcdGroups && open; ++k) {
         const int x = (my_group + k) % kXcdGroups;
         if (!(open & (1u << x))) continue;
-        const int n = chunk_group_heads(a.num_heads, x) * n_tiles;
+        const int n = chunk_group_items(a.num_heads, gsub, n_tiles, x);
         const int c = static_cast<int>(atomicAdd(&a.hdr->chunk_counter[x], 1u));
         if (c < n) {
           s_chunk_open = open;
@@ -1510,6 +1518,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
   };
   auto claim_dec = [&]() -> int {
     if (!s_dec_open) return kDone;
+    // fp32: a relaxed read first closes a drained queue without an atomic --
+    // with few decode items (the worked example has 2), hundreds of workgroups
+    // would otherwise queue failing atomics on this one counter before they
+    // look at the chunk queues.  (Not in the bf16 instances, whose compiled
+    // code it would change; their steps have many decode items.)
+    if (sizeof(T) == 4 &&
+        __hip_atomic_load(&a.hdr->dec_counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+            static_cast<unsigned>(n_dec)) {
+      s_dec_open = 0;
+      return kDone;
+    }
     const int d = static_cast<int>(atomicAdd(&a.hdr->dec_counter, 1u));
     if (d < n_dec) return kDecodeTag | d;
     s_dec_open = 0;
@@ -1524,7 +1543,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
     s_chunk_open = (a.roles & 1) ? (1u << kXcdGroups) - 1 : 0u;
     s_dec_open = (a.roles & 2) ? 1 : 0;
     const int rank = blockIdx.x / kXcdGroups;  // among chunk-first workgroups of this group
-    if (chunk_first && rank < chunk_group_heads(a.num_heads, my_group) * n_tiles)
+    if (chunk_first && rank < chunk_group_items(a.num_heads, gsub, n_tiles, my_group))
       s_next = (my_group << 24) | rank;
     else if (!chunk_first && static_cast<int>(blockIdx.x) - half < n_dec)
       s_next = kDecodeTag | (blockIdx.x - half);
@@ -1550,16 +1569,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
         kind = 2;
       } else if (cur != kDone) {
         // group x holds, segment by segment, (head x + 8k, tile, split) for its
-        // heads; tile_prefix counts (tile, split) pairs
+        // heads; tile_prefix counts (tile, split) pairs.  With gsub > 1 group x
+        // holds pairs x / H, x / H + gsub, ... of head x % H.
         const int x = cur >> 24, i = cur & ((1 << 24) - 1);
-        const int nh = chunk_group_heads(a.num_heads, x);
-        const int t = i / nh;  // pair rank over all segments, scaled down by the group's heads
+        const int nh = gsub > 1 ? 1 : chunk_group_heads(a.num_heads, x);
+        // pair rank over all segments (scaled down by the group's heads)
+        const int t = gsub > 1 ? i * gsub + x / a.num_heads : i / nh;
         seg = lds_lookup ? find_segment_lds(s_prefix[0], a.num_seqs, t)
                          : find_segment(a.tile_prefix, a.num_seqs, t);
         const int t0 = lds_lookup ? s_prefix[0][seg] : a.tile_prefix[seg];
         const int nts = (lds_lookup ? s_prefix[0][seg + 1] : a.tile_prefix[seg + 1]) - t0;
-        const int local = i - nh * t0, r = local % nts;
-        p1 = x + kXcdGroups * (local / nts);  // query head
+        const int local = gsub > 1 ? t - t0 : i - nh * t0, r = local % nts;
+        p1 = gsub > 1 ? x % a.num_heads : x + kXcdGroups * (local / nts);  // query head
         if (csplit == 1) {
           p2 = nts - 1 - r;                   // query tile, longest first
         } else {
@@ -1608,17 +1629,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
 
 // ---------------------------------------------------------------- combine
 // Workgroups past the decode ones merge split chunk tiles: each takes
-// (tile, head) pairs in turn; 4 threads per query row, D / 4 channels each.
-constexpr int kChunkMergeBlocks = 64;
+// (tile, head, 32-row group) units in turn; 8 threads per query row, D / 8
+// channels each.
+constexpr int kChunkMergeBlocks = 256;
 
 template <typename T, int D>
 __device__ void merge_chunk_tiles(const MainArgs& a, int blk) {
   const int S = a.hdr->chunk_split;
   if (S <= 1) return;
-  constexpr int QPR = 4, CPT = D / QPR, NV = CPT / 4;
+  constexpr int QPR = 8, CPT = D / QPR, NV = CPT / 4;
   constexpr int RPB = kThreads / QPR;       // rows of a tile merged by one workgroup pass
   constexpr int GROUPS = kChunkRows / RPB;  // row groups per (tile, head)
-  constexpr int BATCH = 4;                  // key ranges whose partials are loaded together
+  constexpr int BATCH = 8;                  // key ranges whose partials are loaded together
   const int n_pairs = a.hdr->n_chunk_tiles / S * a.num_heads;
   const size_t sstep = static_cast<size_t>(a.num_heads) * kChunkRows * a.part_stride;
   const int c0 = (threadIdx.x % QPR) * CPT;
@@ -1850,12 +1872,16 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
               L.max_blocks, L.num_heads, head_groups, L.ws.parts_cap, grid * kItemsPerSlot,
               grid, L.ws.tiles_cap, split_ok ? L.ws.chunk_slots_cap : 0, chunk_first_wgs,
               dec_first_wgs, split_items, chunk_step_cost, kContig ? L.cu_seqlens_k : nullptr,
-              L.total_k, kContig ? seqlens : nullptr, hdr, tile_prefix, dec_prefix, part_prefix};
+              L.total_k, kContig ? seqlens : nullptr, hdr, tile_prefix, dec_prefix, part_prefix,
+              chunk_group_sub(sizeof(T) == 4, L.num_heads)};
   // hybrid_step_fwd: the append first -- with the small planner in the same
-  // launch when the rows are wide (one workgroup per token), else on its own
+  // launch when the step has few segments, else on its own
   const long long chunks_per_row = static_cast<long long>(L.num_kv_heads) * L.head_dim * sizeof(T) / 16;
+  const long long append_wgs = chunks_per_row >= kThreads / 2
+                                   ? L.total_q
+                                   : (L.total_q * chunks_per_row + kThreads - 1) / kThreads;
   const bool fused_append = L.append_key && L.num_seqs <= kPlanSmallSegments &&
-                            chunks_per_row >= kThreads / 2;
+                            append_wgs < 0x7fffffffLL;
   if (L.append_key && !fused_append) {
     e = launch_kv_append(L.append_key, L.append_value, L.slot_mapping, const_cast<void*>(L.k_cache),
                          const_cast<void*>(L.v_cache), L.total_q, L.num_kv_heads, L.head_dim,
@@ -1866,8 +1892,9 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
     const AppendRows rows{static_cast<const uint4*>(L.append_key), static_cast<const uint4*>(L.append_value),
                           L.slot_mapping, static_cast<uint4*>(const_cast<void*>(L.k_cache)),
                           static_cast<uint4*>(const_cast<void*>(L.v_cache)),
-                          static_cast<int>(chunks_per_row), static_cast<long long>(L.num_blocks) * kPage};
-    hipLaunchKernelGGL(append_plan_kernel, dim3(static_cast<unsigned>(L.total_q) + 1), dim3(kThreads), 0,
+                          static_cast<int>(chunks_per_row), static_cast<long long>(L.num_blocks) * kPage,
+                          L.total_q};
+    hipLaunchKernelGGL(append_plan_kernel, dim3(static_cast<unsigned>(append_wgs) + 1), dim3(kThreads), 0,
                        L.stream, pa, rows);
   } else if (L.num_seqs <= kPlanSmallSegments) {
     hipLaunchKernelGGL(plan_kernel_small, dim3(1), dim3(kWave), 0, L.stream, pa);

@@ -39,6 +39,21 @@ constexpr int kXcdGroups = 8;
 __host__ __device__ inline int chunk_group_heads(int num_heads, int x) {
   return num_heads / kXcdGroups + (x < num_heads % kXcdGroups ? 1 : 0);
 }
+// Chunk items in group x when each of the `pairs` (query tile, key range)
+// pairs of a head is one item.  gsub == 1: the group holds every pair of heads
+// x, x + 8, ...  gsub > 1 (fp32 steps with fewer heads than groups): head
+// x % H deals its pairs over gsub groups, pair t going to group
+// (t % gsub) * H + head, so that every group has work.
+__host__ __device__ inline int chunk_group_items(int num_heads, int gsub, int pairs, int x) {
+  if (gsub <= 1) return chunk_group_heads(num_heads, x) * pairs;
+  if (x >= num_heads * gsub) return 0;
+  const int sub = x / num_heads;
+  return (pairs - sub + gsub - 1) / gsub;
+}
+// Sub-groups per head for a step of num_heads heads (see chunk_group_items).
+__host__ __device__ inline int chunk_group_sub(bool fp32, int num_heads) {
+  return (fp32 && num_heads < kXcdGroups) ? kXcdGroups / num_heads : 1;
+}
 
 struct PlanHeader {
   uint32_t chunk_counter[kXcdGroups];  // next chunk item of each group (set by the planner)
@@ -49,7 +64,8 @@ struct PlanHeader {
   int32_t n_parts;        // partial slots in use
   int32_t bad_segments;   // segments skipped because they broke a precondition
   int32_t chunk_split;    // KV splits per chunk tile (1: tiles are not split)
-  int32_t pad[49];
+  int32_t chunk_gsub;     // queue groups per head (chunk_group_items)
+  int32_t pad[48];
 };
 static_assert(sizeof(PlanHeader) == 256, "header is 256 bytes");
 
@@ -140,7 +156,8 @@ struct AttnLaunch {
 
 // One token row of the append: the row's K and V (chunks_per_row 16-byte
 // chunks each) go to slot slot_mapping[t]; a padding token (slot < 0) or a
-// slot outside the pool is skipped.  Called by one workgroup per token.
+// slot outside the pool is skipped.  append_row: called by one workgroup per
+// token; append_chunk: one thread per 16-byte chunk (short rows).
 struct AppendRows {
   const uint4* key;
   const uint4* value;
@@ -149,7 +166,20 @@ struct AppendRows {
   uint4* v_cache;
   int chunks_per_row;
   long long pool_slots;
+  int total_tokens;
 };
+__device__ __forceinline__ void append_chunk(const AppendRows& a, long long idx) {
+  if (idx >= static_cast<long long>(a.total_tokens) * a.chunks_per_row) return;
+  const int t = static_cast<int>(idx / a.chunks_per_row);
+  const int c = static_cast<int>(idx - static_cast<long long>(t) * a.chunks_per_row);
+  const int slot = a.slot_mapping[t];
+  if (slot < 0 || slot >= a.pool_slots) return;  // padding token or slot outside the pool
+  const size_t dst = static_cast<size_t>(slot) * a.chunks_per_row + c;
+  const uint4 kv = a.key[idx];
+  const uint4 vv = a.value[idx];
+  a.k_cache[dst] = kv;
+  a.v_cache[dst] = vv;
+}
 __device__ __forceinline__ void append_row(const AppendRows& a, int t) {
   const int slot = __builtin_amdgcn_readfirstlane(a.slot_mapping[t]);
   if (slot < 0 || slot >= a.pool_slots) return;

@@ -13,20 +13,8 @@ namespace ha {
 
 // Short rows: one thread moves one 16-byte chunk of K and the same chunk of V.
 // grid.x * blockDim.x >= total_tokens * chunks_per_row (checked by the launcher).
-__global__ __launch_bounds__(kThreads) void kv_append_kernel(
-    const u32x4_t* __restrict__ key, const u32x4_t* __restrict__ value,
-    const int32_t* __restrict__ slot_mapping, u32x4_t* __restrict__ k_cache,
-    u32x4_t* __restrict__ v_cache, int total_tokens, int chunks_per_row, long long pool_slots) {
-  const long long idx = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x;
-  const long long total = static_cast<long long>(total_tokens) * chunks_per_row;
-  if (idx >= total) return;
-  const int t = static_cast<int>(idx / chunks_per_row);
-  const int c = static_cast<int>(idx - static_cast<long long>(t) * chunks_per_row);
-  const int slot = slot_mapping[t];
-  if (slot < 0 || slot >= pool_slots) return;  // padding token or slot outside the pool
-  const size_t dst = static_cast<size_t>(slot) * chunks_per_row + c;
-  k_cache[dst] = key[idx];
-  v_cache[dst] = value[idx];
+__global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendRows a) {
+  append_chunk(a, static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x);
 }
 
 // Rows of at least half a workgroup of chunks (e.g. 32 heads x 128 bf16 = 512):
@@ -45,10 +33,10 @@ hipError_t launch_kv_append(const void* key, const void* value, const int32_t* s
   const long long total = static_cast<long long>(total_tokens) * chunks_per_row;
   if (total == 0) return hipSuccess;
   const long long pool_slots = static_cast<long long>(num_blocks) * kPage;
+  const AppendRows rows{static_cast<const uint4*>(key), static_cast<const uint4*>(value),
+                        slot_mapping, static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache),
+                        chunks_per_row, pool_slots, total_tokens};
   if (chunks_per_row >= kThreads / 2) {
-    const AppendRows rows{static_cast<const uint4*>(key), static_cast<const uint4*>(value),
-                          slot_mapping, static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache),
-                          chunks_per_row, pool_slots};
     hipLaunchKernelGGL(kv_append_rows_kernel, dim3(static_cast<unsigned>(total_tokens)),
                        dim3(kThreads), 0, stream, rows);
     return hipGetLastError();
@@ -56,9 +44,7 @@ hipError_t launch_kv_append(const void* key, const void* value, const int32_t* s
   const long long blocks = (total + kThreads - 1) / kThreads;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kv_append_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                     stream, static_cast<const u32x4_t*>(key), static_cast<const u32x4_t*>(value),
-                     slot_mapping, static_cast<u32x4_t*>(k_cache), static_cast<u32x4_t*>(v_cache),
-                     total_tokens, chunks_per_row, pool_slots);
+                     stream, rows);
   return hipGetLastError();
 }
 
