@@ -54,6 +54,8 @@ SWEEP = [
     # 4 has 2), GQA groups of 2 and of 8
     ([(1, 1), (1, 40), (1, 700), (1, 257), (20, 90)], 6, 3, 128, W.BF16, 15),
     ([(1, 3000), (1, 65), (1, 16), (40, 40)], 16, 2, 64, W.BF16, 16),
+    # fp32 with as many heads as chunk queue groups (one head per group)
+    ([(1, 300), (140, 600), (1, 1), (33, 33)], 8, 8, 64, W.F32, 17),
 ]
 
 
@@ -86,6 +88,8 @@ SPLIT_CASES = [
     ([(300, 3000), (1, 100)], 2, 2, 128, W.F32, 24),
     ([(1, 700), (257, 2900), (1, 33)], 4, 2, 64, W.F32, 25),   # GQA
     ([(77, 5000), (1, 5), (400, 1400)], 2, 2, 128, W.BF16, 26),
+    # fp32, one head: its (tile, range) pairs are dealt over all 8 chunk queues
+    ([(300, 6000), (1, 50), (1, 2)], 1, 1, 64, W.F32, 27),
 ]
 
 
