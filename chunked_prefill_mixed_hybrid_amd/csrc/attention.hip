@@ -1428,7 +1428,10 @@ __device__ __forceinline__ int find_segment_lds(const int* prefix, int n, int x)
 
 // kSplit: this launch may meet split chunk tiles (the planner was allowed to
 // split); the instance without it keeps the unsplit roles' register allocation.
-template <typename T, int D, bool kSplit, bool kContig>
+// kDefer: a chunk item claims its successor only when it is done (else at its
+// start, hiding the atomic's latency).  Chosen by the host per step, so that
+// the steps that do not need it keep the instance tuned without it.
+template <typename T, int D, bool kSplit, bool kContig, bool kDefer>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
   constexpr int kSmem = ChunkCfg<T>::template Sizes<D>::BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kSmem];
@@ -1558,7 +1561,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
   // hang; tests/test_kernel_structure.py checks the compiled loops).
   for (;;) {
     if (threadIdx.x == 0) {
-      if (sizeof(T) == 4 && s_next == kPending) s_next = claim();  // claim deferred by a chunk item
+      if (kDefer && s_next == kPending) s_next = claim();  // claim deferred by a chunk item
       const int cur = s_next;
       int kind = 0, seg = 0, p1 = 0, p2 = 0, p3 = 0;  // kind: 0 done, 1 chunk, 2 decode
       if (cur != kDone && (cur & kDecodeTag)) {
@@ -1605,13 +1608,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
     const int p3 = __builtin_amdgcn_readfirstlane(s_work[4]);
     __syncthreads();
     if (kind == 0) break;
-    // the next item, claimed while this one runs (hides the atomic's latency).
-    // fp32 chunk items are claimed only once done: in the fp32 worked-example
-    // shape there are about as many items as workgroups, and an item reserved
-    // at the start of a long chunk tile waits behind it while other workgroups
-    // run dry.  (bf16 instances keep the early claim: the deferred one costs
-    // them register spills.)
-    if (threadIdx.x == 0) s_next = (sizeof(T) == 4 && kind == 1) ? kPending : claim();
+    // the next item, claimed while this one runs (hides the atomic's latency),
+    // or with kDefer, after a chunk item only once it is done: an item
+    // reserved at the start of a long chunk tile waits behind it while other
+    // workgroups run dry
+    if (threadIdx.x == 0) s_next = (kDefer && kind == 1) ? kPending : claim();
     if (kind == 1) {
       if (csplit == 1) {
         if constexpr (sizeof(T) == 2) chunk_tile_bf16<D, false, kContig>(a, seg, p1, p2, 0, 1, smem);
@@ -1814,19 +1815,20 @@ hipError_t side_stream(int dev, SideStream*& out) {
   return hipSuccess;
 }
 
-template <typename T, int D, bool kSplit, bool kContig>
+template <typename T, int D, bool kSplit, bool kContig, bool kDefer>
 void launch_attn(const MainArgs& ma, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_kernel<T, D, kSplit, kContig>), dim3(grid), dim3(kThreads), 0, st, ma);
+  hipLaunchKernelGGL((attn_kernel<T, D, kSplit, kContig, kDefer>), dim3(grid), dim3(kThreads), 0, st, ma);
 }
 
 template <typename T, int D, bool kContig>
 hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
+  constexpr bool kF32 = sizeof(T) == 4;
   // Chunk tiles may be split only when even the largest number of them the
   // bounds allow (tiles_cap per head) fills at most half of split_items; every
   // other step runs the instance without the split code.
   int grid = 0;
   hipError_t e = occupancy(info, dt, di, 0,
-                           reinterpret_cast<const void*>(attn_kernel<T, D, false, kContig>), grid);
+                           reinterpret_cast<const void*>(attn_kernel<T, D, false, kContig, kF32>), grid);
   if (e != hipSuccess) return e;
   // For bf16, splitting pays only while it brings idle CUs into use: a second
   // item on a CU shares its MFMA and LDS with the first (measured: a bf16 chunk
@@ -1838,7 +1840,7 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
   const bool split_ok = L.ws.chunk_slots_cap >= 2 &&
                         2LL * L.ws.tiles_cap * L.num_heads <= static_cast<long long>(split_items);
   if (split_ok) {
-    e = occupancy(info, dt, di, 1, reinterpret_cast<const void*>(attn_kernel<T, D, true, kContig>), grid);
+    e = occupancy(info, dt, di, 1, reinterpret_cast<const void*>(attn_kernel<T, D, true, kContig, kF32>), grid);
     if (e != hipSuccess) return e;
   }
   SideStream* side = nullptr;
@@ -1909,7 +1911,17 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
               tile_prefix, dec_prefix, part_prefix,
               reinterpret_cast<float*>(ws + L.ws.partials),
               reinterpret_cast<float*>(ws + L.ws.chunk_partials), L.cu_seqlens_k, 3, half};
-  auto attn = split_ok ? launch_attn<T, D, true, kContig> : launch_attn<T, D, false, kContig>;
+  // Deferred chunk claims (kDefer): always for fp32; for bf16 when the longest
+  // chunk alone has more tiles than the grid has workgroups, so that chunk-first
+  // workgroups run several chunk items each and an early claim would reserve
+  // a chunk item behind a chunk item (budget-2048 step: 3157 -> 3035 us).  In
+  // the other bf16 steps chunk-first workgroups reserve decode items, and the
+  // instance without it is faster (mixed bench step: 3.5 us).
+  const bool defer = kF32 || static_cast<long long>((L.max_seqlen_q + kChunkRows - 1) / kChunkRows) *
+                                     L.num_heads > grid;
+  auto attn = split_ok ? launch_attn<T, D, true, kContig, kF32>
+                       : (defer ? launch_attn<T, D, false, kContig, true>
+                                : launch_attn<T, D, false, kContig, kF32>);
   if (L.launch_mode == kLaunchFused) {
     attn(ma, grid, L.stream);
   } else {

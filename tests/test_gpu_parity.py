@@ -56,6 +56,9 @@ SWEEP = [
     ([(1, 3000), (1, 65), (1, 16), (40, 40)], 16, 2, 64, W.BF16, 16),
     # fp32 with as many heads as chunk queue groups (one head per group)
     ([(1, 300), (140, 600), (1, 1), (33, 33)], 8, 8, 64, W.F32, 17),
+    # bf16 chunk with more tiles (9 x 64 heads) than the grid has workgroups:
+    # the instance whose chunk items claim their successor when done
+    ([(1100, 1200), (1, 700), (1, 33)], 64, 64, 128, W.BF16, 18),
 ]
 
 
