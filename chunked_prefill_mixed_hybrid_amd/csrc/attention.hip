@@ -462,6 +462,10 @@ __device__ __forceinline__ int segment_row0(const MainArgs& a, int seg) {
   else return 0;
 }
 
+// s_waitcnt operand (gfx9 encoding) that waits for every outstanding vector
+// memory load and nothing else: vmcnt 0, expcnt 7, lgkmcnt 15.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // XOR swizzle (in 16-byte chunks of 8 keys) of row d of the transposed V tile.
 __device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
 constexpr uint32_t kBf16PairOne = 0x3f803f80u;  // (1.0, 1.0) as a bf16 pair
@@ -530,7 +534,7 @@ __device__ __forceinline__ void chunk_store_partial(const MainArgs& a, int seg, 
 // ---------------------------------------------------------------- chunk role, bf16
 // kSplit: the tile is one of nsplit key ranges (else nsplit == 1, split == 0);
 // kContig: keys in a packed buffer instead of pages
-template <int D, bool kSplit, bool kContig>
+template <int D, bool kSplit, bool kContig, bool kQWait>
 __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, int split, int nsplit,
                                 unsigned char* smem) {
   if constexpr (!kSplit) {
@@ -568,6 +572,10 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, int
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = ok ? ld16(qp + s * 16) : u32x4_t{0, 0, 0, 0};
   }
+  // kQWait: wait for the Q loads here, once per tile.  Left pending into the
+  // key loop, they make the compiler wait for every outstanding global load
+  // (the next tiles' K/V prefetch included) before each step's first MFMA.
+  if constexpr (kQWait) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   f32x16_t acc[NM];
 #pragma unroll
@@ -1615,10 +1623,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
     if (threadIdx.x == 0) s_next = (kDefer && kind == 1) ? kPending : claim();
     if (kind == 1) {
       if (csplit == 1) {
-        if constexpr (sizeof(T) == 2) chunk_tile_bf16<D, false, kContig>(a, seg, p1, p2, 0, 1, smem);
+        if constexpr (sizeof(T) == 2) chunk_tile_bf16<D, false, kContig, kDefer>(a, seg, p1, p2, 0, 1, smem);
         else chunk_tile_f32<D, false, kContig>(a, seg, p1, p2, 0, 1, smem);
       } else if constexpr (kSplit) {
-        if constexpr (sizeof(T) == 2) chunk_tile_bf16<D, true, kContig>(a, seg, p1, p2, p3, csplit, smem);
+        if constexpr (sizeof(T) == 2) chunk_tile_bf16<D, true, kContig, kDefer>(a, seg, p1, p2, p3, csplit, smem);
         else chunk_tile_f32<D, true, kContig>(a, seg, p1, p2, p3, csplit, smem);
       }
     } else {
