@@ -88,7 +88,7 @@ __device__ __forceinline__ bool plan_segment(const PlanArgs& a, int b, int& lq, 
 // an even share of the whole step's work; then every chunk tile is cut into S
 // ranges, within the item, slot and minimum-length limits.
 __device__ int chunk_split_count(const PlanArgs& a, long long csteps, long long dkeys,
-                                 long long n_ct, long long steps_max) {
+                                 long long n_ct, long long steps_max, bool cap_items = true) {
   int S = 1;
   if (n_ct > 0 && n_ct <= a.tiles_cap && a.chunk_slots_cap >= 2) {
     const double work = (static_cast<double>(csteps) * a.chunk_step_cost +
@@ -97,8 +97,10 @@ __device__ int chunk_split_count(const PlanArgs& a, long long csteps, long long 
     const double longest = static_cast<double>(steps_max) * a.chunk_step_cost;
     if (longest > share) {
       long long want = static_cast<long long>(ceil(longest / share));
-      want = min(want, static_cast<long long>(a.split_items) / (n_ct * a.num_heads));
-      want = min(want, static_cast<long long>(kChunkSplitItems) / (n_ct * a.num_heads));
+      if (cap_items) {  // every (tile, range) pair counted as an item
+        want = min(want, static_cast<long long>(a.split_items) / (n_ct * a.num_heads));
+        want = min(want, static_cast<long long>(kChunkSplitItems) / (n_ct * a.num_heads));
+      }
       want = min(want, static_cast<long long>(a.chunk_slots_cap) / n_ct);
       want = min(want, steps_max * 64 / kChunkSplitMinKeys);
       S = static_cast<int>(max(want, 1LL));
@@ -181,7 +183,34 @@ __device__ __forceinline__ void plan_small(const PlanArgs& a) {  // the 64 lanes
     ctiles += __shfl_xor(ctiles, m);
     cmax = max(cmax, __shfl_xor(cmax, m));
   }
-  const int csplit = chunk_split_count(a, csteps, dkeys, ctiles, cmax);
+  // chunk split: the largest count whose non-empty (tile, range) items fit the
+  // item limits; ranges of a segment are of equal length (chunk_key_range), so
+  // tiles with fewer keys have fewer non-empty ranges
+  int csplit = chunk_split_count(a, csteps, dkeys, ctiles, cmax, false);
+  while (csplit > 1) {
+    long long n = 0;
+    if (lq >= 2) {
+      // sum over tiles of ceil(kend / ck): the full tiles' ends step by 128,
+      // so the quotient is carried along instead of divided out per tile
+      const int ck = chunk_range_keys(lk, csplit);
+      const int full = (lq - 1) / kChunkRows;  // tiles before the last
+      int q = (lk - lq + kChunkRows + ck - 1) / ck, rr = (lk - lq + kChunkRows + ck - 1) - q * ck;
+      for (int t = 0; t < full; ++t) {
+        n += q;
+        rr += kChunkRows;
+        while (rr >= ck) {
+          rr -= ck;
+          ++q;
+        }
+      }
+      n += (lk + ck - 1) / ck;  // the last tile ends at lk
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) n += __shfl_xor(n, m);
+    if (n * a.num_heads <= min(static_cast<long long>(a.split_items), static_cast<long long>(kChunkSplitItems)))
+      break;
+    --csplit;
+  }
   const int split_log = kSplitMinLog2 + pick;
   const int split = 1 << split_log;
   // exclusive prefix sums over the lanes
@@ -495,17 +524,16 @@ template <int NCH>
 __device__ __forceinline__ int vt_swz_f32(int d) { return (d ^ (d >> 2)) & (NCH - 1); }
 
 // ---------------------------------------------------------------- chunk KV splits
-// Keys [kb0, kb1) of split `split` out of `nsplit` of a chunk tile whose keys
-// are [0, kend): equal ranges rounded up to 64 keys, so every range boundary
-// other than kend falls on a 64-key step (keys past a range end are never
-// loaded and never need a mask).  Late ranges of short tiles may be empty.
-__device__ __forceinline__ void chunk_key_range(int kend, int split, int nsplit, int& kb0, int& kb1) {
+// Keys [kb0, kb1) of range `split` out of `nsplit` of a chunk tile whose keys
+// are [0, kend) in a segment of lk keys: the segment's ranges cut at the
+// tile's end, so the late ranges of tiles with fewer keys are empty.
+__device__ __forceinline__ void chunk_key_range(int lk, int kend, int split, int nsplit, int& kb0, int& kb1) {
   if (nsplit == 1) {
     kb0 = 0;
     kb1 = kend;
     return;
   }
-  const int ck = ((kend + nsplit - 1) / nsplit + 63) & ~63;
+  const int ck = chunk_range_keys(lk, nsplit);
   kb0 = min(split * ck, kend);
   kb1 = min(kb0 + ck, kend);
 }
@@ -557,7 +585,7 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, int
   const int rows_end = min(row0 + kChunkRows, Lq);
   const int kend = H0 + rows_end;  // keys [0, kend) are visible to some row of the tile
   int kb0, kb1;                    // this item's keys
-  chunk_key_range(kend, split, nsplit, kb0, kb1);
+  chunk_key_range(Lk, kend, split, nsplit, kb0, kb1);
   const int wrow0 = row0 + w * 32;
   const int my_row = wrow0 + qc;
   const bool wave_active = wrow0 < rows_end;
@@ -811,7 +839,7 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, int 
   const int rows_end = min(row0 + kChunkRows, Lq);
   const int kend = H0 + rows_end;
   int kb0, kb1;  // this item's keys
-  chunk_key_range(kend, split, nsplit, kb0, kb1);
+  chunk_key_range(Lk, kend, split, nsplit, kb0, kb1);
   const int wrow0 = row0 + w * 32;
   const int my_row = wrow0 + qc;
   const bool wave_active = wrow0 < rows_end;
@@ -1595,8 +1623,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
         if (csplit == 1) {
           p2 = nts - 1 - r;                   // query tile, longest first
         } else {
-          p2 = nts / csplit - 1 - r / csplit;
-          p3 = r % csplit;                    // key range of the tile
+          // range-major: the first range of every tile before any second
+          // range, so the short and empty last ranges are handed out last
+          const int ntl = nts / csplit;
+          p3 = r / ntl;                       // key range of the tile
+          p2 = ntl - 1 - (r - p3 * ntl);      // query tile, longest first
         }
         kind = 1;
       }

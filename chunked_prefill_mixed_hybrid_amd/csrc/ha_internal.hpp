@@ -21,9 +21,19 @@ constexpr int kHeadsPerDecodeItem = 4;  // bf16: one head per 16-lane row of eve
 constexpr int kMaxSeqlenK = 1 << 30;
 // Chunk tiles are split along the keys only when a few long tiles would
 // otherwise outlast the rest of the step: at most this many (tile, head, split)
-// items in all, each split at least kChunkSplitMinKeys keys long.
+// items in all (kChunkSplitItems; the one-wave planner counts only non-empty
+// ranges against it), each range at least kChunkSplitMinKeys keys long, with
+// partial slots for up to kChunkSlotItems (tile, head, range) triples.
 constexpr int kChunkSplitItems = 512;
+constexpr int kChunkSlotItems = 1024;
 constexpr int kChunkSplitMinKeys = 512;
+// Length of each of the nsplit key ranges of a split chunk segment of lk keys:
+// equal ranges rounded up to 64 keys, so every range boundary other than a
+// tile's end falls on a 64-key step (keys past a range end are never loaded and
+// never need a mask).
+__host__ __device__ inline int chunk_range_keys(int lk, int nsplit) {
+  return ((lk + nsplit - 1) / nsplit + 63) & ~63;
+}
 
 // ---- workspace ---------------------------------------------------------------------
 // [header 256 B][tile_prefix (B+1)][dec_prefix (B+1)][part_prefix (B+1)][seqlens (B+1)]
@@ -93,7 +103,7 @@ inline int tiles_cap_for(int num_seqs, int total_q) {
 }
 
 inline int chunk_slots_cap_for(int num_seqs, int total_q, int max_seqlen_k, int num_heads) {
-  const long long by_items = kChunkSplitItems / num_heads;
+  const long long by_items = kChunkSlotItems / num_heads;
   const long long max_split = (static_cast<long long>(max_seqlen_k) + kChunkSplitMinKeys - 1) /
                               kChunkSplitMinKeys;
   const long long by_shape = static_cast<long long>(tiles_cap_for(num_seqs, total_q)) * max_split;
