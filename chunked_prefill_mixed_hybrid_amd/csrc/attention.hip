@@ -922,12 +922,17 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, int 
       for (int kb = 0; kb < NKB; ++kb) {
         sacc[kb] = f32x16_t{};
         const float* kr = Ks + (kb * 32 + pi) * ROWF + g * KS;
+        // all of the block's K operands first: the reads overlap each other and
+        // the previous block's MFMAs instead of one read latency per 4 MFMAs
+        f32x4_t kf[KS / 4];
 #pragma unroll
-        for (int s = 0; s < KS; s += 4) {
-          const f32x4_t kf = *reinterpret_cast<const f32x4_t*>(kr + s);
+        for (int s4 = 0; s4 < KS / 4; ++s4) kf[s4] = *reinterpret_cast<const f32x4_t*>(kr + 4 * s4);
+        // keep the reads ahead of the MFMAs (at D = 128 the held operands would spill)
+        if constexpr (D == 64) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sacc[kb] = mfma_f32(kf[e], qf[s + e], sacc[kb]);
-        }
+        for (int s4 = 0; s4 < KS / 4; ++s4)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sacc[kb] = mfma_f32(kf[s4][e], qf[4 * s4 + e], sacc[kb]);
       }
       float tmax = -INFINITY;
 #pragma unroll
@@ -967,21 +972,28 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, int 
       // i.e. 16-byte V^T chunk kb*8 + 4 (n/8) + 2 g + (n % 8) / 4
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
+        // the block's V^T operands first (2 halves x NM channel blocks x 2 chunks)
+        f32x4_t vf[2][NM][2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int m = 0; m < NM; ++m) {
             const int d = m * 32 + qc;
             const float* vrow = Vt + d * BN;
             const int ch = kb * 8 + 4 * u + 2 * g, sw = vt_swz_f32<NCH>(d);
-            const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(vrow + 4 * (ch ^ sw));
-            const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(vrow + 4 * ((ch + 1) ^ sw));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[m] = mfma_f32(v0[e], sacc[kb][8 * u + e], acc[m]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[m] = mfma_f32(v1[e], sacc[kb][8 * u + 4 + e], acc[m]);
+            vf[u][m][0] = *reinterpret_cast<const f32x4_t*>(vrow + 4 * (ch ^ sw));
+            vf[u][m][1] = *reinterpret_cast<const f32x4_t*>(vrow + 4 * ((ch + 1) ^ sw));
           }
-        }
+        if constexpr (D == 64) __builtin_amdgcn_sched_barrier(0);  // as for K
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                acc[m] = mfma_f32(vf[u][m][h2][e], sacc[kb][8 * u + 4 * h2 + e], acc[m]);
       }
     }
     if (k0 + BN < kb1) {
