@@ -1965,9 +1965,10 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
   // Deferred chunk claims (kDefer): always for fp32; for bf16 when the longest
   // chunk alone has more tiles than the grid has workgroups, so that chunk-first
   // workgroups run several chunk items each and an early claim would reserve
-  // a chunk item behind a chunk item (budget-2048 step: 3157 -> 3035 us).  In
-  // the other bf16 steps chunk-first workgroups reserve decode items, and the
-  // instance without it is faster (mixed bench step: 3.5 us).
+  // a chunk item behind a chunk item (a 1984-token chunk + 64 decodes, 64
+  // heads: 3157 -> 3035 us).  In the other bf16 steps chunk-first workgroups
+  // reserve decode items, and the instance without it is faster (two 512-token
+  // chunks + 30 decodes, 32 heads: by 3.5 us).
   const bool defer = kF32 || static_cast<long long>((L.max_seqlen_q + kChunkRows - 1) / kChunkRows) *
                                      L.num_heads > grid;
   auto attn = split_ok ? launch_attn<T, D, true, kContig, kF32>
