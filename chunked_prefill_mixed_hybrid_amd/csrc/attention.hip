@@ -1681,7 +1681,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
 
 // ---------------------------------------------------------------- combine
 // Workgroups past the decode ones merge split chunk tiles: each takes
-// (tile, head, 32-row group) units in turn; 8 threads per query row, D / 8
+// (tile, head, 16-row group) units in turn; 16 threads per query row, D / 16
 // channels each.
 constexpr int kChunkMergeBlocks = 256;
 
@@ -1689,10 +1689,10 @@ template <typename T, int D>
 __device__ void merge_chunk_tiles(const MainArgs& a, int blk) {
   const int S = a.hdr->chunk_split;
   if (S <= 1) return;
-  constexpr int QPR = 8, CPT = D / QPR, NV = CPT / 4;
+  constexpr int QPR = 16, CPT = D / QPR, NV = CPT / 4;
   constexpr int RPB = kThreads / QPR;       // rows of a tile merged by one workgroup pass
   constexpr int GROUPS = kChunkRows / RPB;  // row groups per (tile, head)
-  constexpr int BATCH = 8;                  // key ranges whose partials are loaded together
+  constexpr int BATCH = 16;                 // key ranges whose partials are loaded together
   const int n_pairs = a.hdr->n_chunk_tiles / S * a.num_heads;
   const size_t sstep = static_cast<size_t>(a.num_heads) * kChunkRows * a.part_stride;
   const int c0 = (threadIdx.x % QPR) * CPT;
