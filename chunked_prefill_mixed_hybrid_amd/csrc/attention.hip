@@ -845,7 +845,9 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, int 
   const bool wave_active = wrow0 < rows_end;
   const int pi = key_perm(qc);
 
-  float qf[KS];  // lane supplies Q[my_row][g * KS + s]
+  // lane supplies Q[my_row][g * KS + s] * scale * log2(e): the scores come out
+  // of the MFMAs already in the base-2 units of the softmax
+  float qf[KS];
   {
     const bool ok = my_row < Lq;
     const float* qp = static_cast<const float*>(a.q) +
@@ -854,7 +856,7 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, int 
     for (int s = 0; s < KS; s += 4) {
       const f32x4_t v = ok ? *reinterpret_cast<const f32x4_t*>(qp + s) : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qf[s + e] = v[e];
+      for (int e = 0; e < 4; ++e) qf[s + e] = v[e] * a.scale_log2;
     }
   }
   f32x16_t acc[NM];
@@ -939,7 +941,7 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, int 
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          float x = sacc[kb][v] * a.scale_log2;
+          float x = sacc[kb][v];
           if (need_mask) {
             const int kp = k0 + kb * 32 + ((v >> 3) << 4) + (g << 3) + (v & 7);
             if (kp > H0 + my_row) x = -INFINITY;
