@@ -931,10 +931,12 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, int 
         for (int s4 = 0; s4 < KS / 4; ++s4) kf[s4] = *reinterpret_cast<const f32x4_t*>(kr + 4 * s4);
         // keep the reads ahead of the MFMAs (at D = 128 the held operands would spill)
         if constexpr (D == 64) __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);  // MFMA clusters issue ahead of the other wave's softmax
 #pragma unroll
         for (int s4 = 0; s4 < KS / 4; ++s4)
 #pragma unroll
           for (int e = 0; e < 4; ++e) sacc[kb] = mfma_f32(kf[s4][e], qf[4 * s4 + e], sacc[kb]);
+        __builtin_amdgcn_s_setprio(0);
       }
       float tmax = -INFINITY;
 #pragma unroll
@@ -987,6 +989,7 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, int 
             vf[u][m][1] = *reinterpret_cast<const f32x4_t*>(vrow + 4 * ((ch + 1) ^ sw));
           }
         if constexpr (D == 64) __builtin_amdgcn_sched_barrier(0);  // as for K
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -996,6 +999,7 @@ __device__ void chunk_tile_f32(const MainArgs& a, int seg, int h, int tile, int 
 #pragma unroll
               for (int e = 0; e < 4; ++e)
                 acc[m] = mfma_f32(vf[u][m][h2][e], sacc[kb][8 * u + 4 * h2 + e], acc[m]);
+        __builtin_amdgcn_s_setprio(0);
       }
     }
     if (k0 + BN < kb1) {
