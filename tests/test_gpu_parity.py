@@ -121,7 +121,9 @@ def test_chunk_split(case):
 # two streams): the same plan and items as the fused launch, so the output is
 # bitwise the fused one.
 TWO_LAUNCH_CASES = [("sweep", 3), ("sweep", 6), ("sweep", 9), ("sweep", 11), ("split", 3),
-                    ("split", 5)]
+                    ("split", 5),
+                    ("sweep", 17),  # bf16 instance with deferred chunk claims
+                    ("split", 6)]   # fp32, one head: queue sub-groups, equal key ranges
 
 
 @pytest.mark.parametrize("two_streams", [False, True])
@@ -167,7 +169,8 @@ def test_two_launch_config2_matches_fused():
 # byte-identical to it.
 CONTIG_CASES = [("sweep", 0), ("sweep", 3), ("sweep", 4), ("sweep", 6), ("sweep", 7),
                 ("sweep", 9), ("sweep", 10), ("sweep", 11), ("sweep", 12), ("sweep", 13),
-                ("sweep", 14), ("sweep", 15), ("split", 1)]
+                ("sweep", 14), ("sweep", 15), ("split", 1),
+                ("sweep", 17), ("split", 3), ("split", 6)]
 
 
 @pytest.mark.parametrize("case", range(len(CONTIG_CASES)))
