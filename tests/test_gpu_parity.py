@@ -93,6 +93,8 @@ SPLIT_CASES = [
     ([(77, 5000), (1, 5), (400, 1400)], 2, 2, 128, W.BF16, 26),
     # fp32, one head: its (tile, range) pairs are dealt over all 8 chunk queues
     ([(300, 6000), (1, 50), (1, 2)], 1, 1, 64, W.F32, 27),
+    # fp32, three heads: two sub-groups per head, two of the eight queues empty
+    ([(600, 4000), (1, 77), (129, 129)], 3, 3, 64, W.F32, 28),
 ]
 
 
