@@ -63,6 +63,9 @@ struct PlanArgs {
   int32_t* dec_prefix;
   int32_t* part_prefix;
   int chunk_gsub;  // queue groups per head (chunk_group_items)
+  // decode-first workgroups left without a decode item take their first chunk
+  // item statically as well (fused fp32 launches, see attn_kernel)
+  int spare_chunk;
 };
 
 constexpr int kPlanThreads = 1024;
@@ -126,9 +129,10 @@ __device__ void write_plan_header(const PlanArgs& a, int chunk_pairs, int dec_it
   a.hdr->chunk_gsub = a.chunk_gsub;
   a.hdr->bad_segments = bad;
   const int cw = a.chunk_first_wgs;
+  const int dec_static = min(dec_items, a.dec_first_wgs);
   for (int x = 0; x < kXcdGroups; ++x) {
     const int items = chunk_group_items(a.num_heads, a.chunk_gsub, chunk_pairs, x);
-    const int first = x < cw ? (cw - x + kXcdGroups - 1) / kXcdGroups : 0;
+    const int first = static_chunk_ranks(cw, dec_static, a.grid, a.spare_chunk != 0, x);
     a.hdr->chunk_counter[x] = static_cast<uint32_t>(min(items, first));
   }
   a.hdr->dec_counter = static_cast<uint32_t>(min(dec_items, a.dec_first_wgs));
@@ -1604,7 +1608,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
       s_next = (my_group << 24) | rank;
     else if (!chunk_first && static_cast<int>(blockIdx.x) - half < n_dec)
       s_next = kDecodeTag | (blockIdx.x - half);
-    else
+    else if constexpr (sizeof(T) == 4) {
+      // fused launch: a decode-first workgroup with no decode item takes the
+      // next static rank of its own group, after the chunk-first ones (the
+      // planner starts the counters past these too), instead of queueing an
+      // atomic on the shared counters (the worked example's 254 such
+      // workgroups started their first item 8 us late)
+      int it = kDone;
+      if (!chunk_first && a.roles == 3) {
+        const int r = spare_chunk_rank(static_cast<int>(blockIdx.x), half, n_dec);
+        if (r < chunk_group_items(a.num_heads, gsub, n_tiles, my_group)) it = (my_group << 24) | r;
+      }
+      s_next = it == kDone ? claim() : it;
+    } else
       s_next = claim();
   }
   __syncthreads();  // LDS prefix copy complete
@@ -1932,7 +1948,8 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
               grid, L.ws.tiles_cap, split_ok ? L.ws.chunk_slots_cap : 0, chunk_first_wgs,
               dec_first_wgs, split_items, chunk_step_cost, kContig ? L.cu_seqlens_k : nullptr,
               L.total_k, kContig ? seqlens : nullptr, hdr, tile_prefix, dec_prefix, part_prefix,
-              chunk_group_sub(sizeof(T) == 4, L.num_heads)};
+              chunk_group_sub(sizeof(T) == 4, L.num_heads),
+              sizeof(T) == 4 && L.launch_mode == kLaunchFused ? 1 : 0};
   // hybrid_step_fwd: the append first -- with the small planner in the same
   // launch when the step has few segments, else on its own
   const long long chunks_per_row = static_cast<long long>(L.num_kv_heads) * L.head_dim * sizeof(T) / 16;

@@ -60,6 +60,25 @@ __host__ __device__ inline int chunk_group_items(int num_heads, int gsub, int pa
   const int sub = x / num_heads;
   return (pairs - sub + gsub - 1) / gsub;
 }
+// Workgroups b < n with b % kXcdGroups == x (the ones whose first items come
+// from queue group x, the group of their own XCD).
+__host__ __device__ constexpr int wgs_in_group(int n, int x) {
+  return n > x ? (n - x + kXcdGroups - 1) / kXcdGroups : 0;
+}
+// Static first chunk items of a fused launch of `grid` workgroups: chunk-first
+// workgroup b < half takes rank b / kXcdGroups of group b % kXcdGroups; with
+// `spare`, a decode-first workgroup b >= half + n_dec (n_dec: decode items,
+// at most grid - half) has no decode item and takes the next rank of its group.
+__host__ __device__ inline int spare_chunk_rank(int b, int half, int n_dec) {
+  const int x = b % kXcdGroups;
+  return wgs_in_group(half, x) + b / kXcdGroups - wgs_in_group(half + n_dec, x);
+}
+// Ranks 0 .. this - 1 of group x are handed out statically (before the cap by
+// the group's items): the group's counter starts there.
+__host__ __device__ inline int static_chunk_ranks(int half, int n_dec, int grid, bool spare, int x) {
+  const int n = wgs_in_group(half, x);
+  return spare ? n + wgs_in_group(grid, x) - wgs_in_group(half + n_dec, x) : n;
+}
 // Sub-groups per head for a step of num_heads heads (see chunk_group_items).
 __host__ __device__ inline int chunk_group_sub(bool fp32, int num_heads) {
   return (fp32 && num_heads < kXcdGroups) ? kXcdGroups / num_heads : 1;

@@ -43,6 +43,30 @@ int main() {
       }
     }
   }
+  // static first chunk items of a fused launch: in every queue group the ranks
+  // of the chunk-first workgroups, then (spare) of the decode-first ones left
+  // without a decode item, are distinct and are exactly 0 .. static_chunk_ranks - 1
+  for (int grid = 1; grid <= 600; grid += (grid < 40 ? 1 : 13)) {
+    const int half = (grid + 1) / 2;
+    for (int n_dec = 0; n_dec <= grid; n_dec += (n_dec < 20 ? 1 : 7)) {
+      const int ds = n_dec < grid - half ? n_dec : grid - half;
+      for (int spare = 0; spare < 2; ++spare) {
+        std::vector<std::vector<int>> seen(kXcdGroups, std::vector<int>(grid + 1, 0));
+        for (int b = 0; b < grid; ++b) {
+          int r = -1;
+          if (b < half) r = b / kXcdGroups;
+          else if (spare && b >= half + ds) r = spare_chunk_rank(b, half, ds);
+          if (r < 0) continue;
+          if (r > grid || seen[b % kXcdGroups][r]++) return fail("static chunk rank repeated", grid, n_dec, b);
+        }
+        for (int x = 0; x < kXcdGroups; ++x) {
+          const int n = static_chunk_ranks(half, ds, grid, spare != 0, x);
+          for (int r = 0; r <= grid; ++r)
+            if (seen[x][r] != (r < n ? 1 : 0)) return fail("static chunk ranks not 0 .. first - 1", grid, n_dec, x);
+        }
+      }
+    }
+  }
   // equal key ranges: 64-aligned, cover the segment, the shortest such length
   for (int lk = 1; lk <= 20000; lk += 7) {
     for (int s = 2; s <= 40; ++s) {
