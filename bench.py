@@ -1,16 +1,23 @@
 """Benchmark of one mixed chunked-prefill step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4] [--extra 1,2,3,5a,5b]
 
 A step is the append of the new tokens' K/V followed by the attention over one
 synthetic batch already resident in HBM: one hybrid_step_fwd call (default), or
-paged_kv_append then hybrid_attn_fwd (--entry calls).  Default workload: 2
-prefill chunks of 512 (histories 0 and 1536) + 30 decodes with history
-U[512, 4096], 32 heads x 128, bf16, 16-token pages, shuffled block ids.  Prints
-ONE JSON line: microseconds per step, the fraction of the step roofline
-max(FLOPs / MFMA peak, bytes / HBM peak), a roofline object for the timed call
-(HIP events on the stream it runs on) and the CPU oracle's time on the host
-cores as a baseline.
+paged_kv_append then hybrid_attn_fwd (--entry calls).  The headline workload
+is the largest single-GPU step: a chunk of 1024 tokens at history 130048 of a
+131072-token prompt plus 64 decodes with history U[8192, 131072], 32 heads x
+128, bf16, 16-token pages, shuffled block ids (75 GB of pages).
+
+Timed region: K steps on one stream, each preceded by a 1 GiB write that
+evicts L2 and the 256 MB MALL (cold, as a serving step meets its KV), each
+bracketed by HIP events; `value` is the median step in microseconds.  Also
+reported: the same steps back to back (warm), the fraction of the step roofline
+max(FLOPs / MFMA peak, bytes / HBM peak), a roofline object for the attention
+call (HIP events on the stream its kernels run on), the CPU oracle's time on
+the host cores as a baseline (a bounded sample of the step, scaled by the
+number of (query, key) pairs), and the other workloads' cold and warm times.
+Prints ONE JSON line.
 """
 from __future__ import annotations
 
@@ -25,6 +32,7 @@ import numpy as np
 METRIC = "µs per mixed step + KV GB/s & TFLOP/s as % of step roofline (1 MI355X)"
 PEAK_HBM_GBS = 8000.0
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+FLUSH_BYTES = 1 << 30
 
 
 def algorithmic_work(meta, spec):
@@ -48,19 +56,24 @@ def algorithmic_work(meta, spec):
     attn_bytes = kv_bytes + qo_bytes + 4.0 * (float(((lk + 15) // 16).sum()) + 2 * b + 1)
     return {"flops": flops, "kv_bytes": kv_bytes, "attn_bytes": attn_bytes,
             "append_bytes": append_bytes + 4.0 * t,
-            "step_bytes": kv_bytes + qo_bytes + append_bytes + meta_bytes}
+            "step_bytes": kv_bytes + qo_bytes + append_bytes + meta_bytes,
+            "pairs": vis}
 
 
-def profiled_traffic(workload_name, unit):
-    """HBM bytes per timed call (unit "step": hybrid_step_fwd; "attn": the
-    attention call) from the committed rocprofv3 counter summary of this
-    workload, or None when there is none or the kernel sources changed since
-    the counters were taken."""
+def step_roofline_us(w, spec):
+    t_mfma = w["flops"] / (PEAK_MFMA_TFLOPS[spec.dtype] * 1e12) * 1e6
+    t_hbm = w["step_bytes"] / (PEAK_HBM_GBS * 1e9) * 1e6
+    return max(t_mfma, t_hbm), ("mfma" if t_mfma > t_hbm else "hbm")
+
+
+def profiled_traffic(workload_name):
+    """HBM bytes per attention call from the committed rocprofv3 counter
+    summary of this workload, or None when there is none or the kernel sources
+    changed since the counters were taken."""
     import hashlib
     from pathlib import Path
     root = Path(__file__).resolve().parent
-    name = f"step_{workload_name}" if unit == "step" else f"attn_kernel_{workload_name}"
-    prof = root / "profiles" / f"{name}.txt"
+    prof = root / "profiles" / f"attn_kernel_{workload_name}.txt"
     if not prof.exists():
         return None
     fields = dict(line.split(": ", 1) for line in prof.read_text().splitlines()
@@ -73,37 +86,236 @@ def profiled_traffic(workload_name, unit):
     return float(fields["traffic_bytes"])
 
 
-def cpu_baseline(ds, spec, meta, budget_s=10.0):
-    """The oracle (as it stands) on the host cores: the whole step (append +
-    attention for every row), repeated until about budget_s of CPU time."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(ds, spec, meta, w, budget_s=15.0, max_host_bytes=6 << 30, target_pairs_heads=2.5e9):
+    """The oracle (as it stands) on the host cores.  Steps whose pages fit
+    max_host_bytes and whose work is small run whole (append + every row);
+    bigger ones run a bounded sample -- evenly spaced rows of the chunk
+    segments plus a seeded subset of the decode segments, pages within
+    max_host_bytes -- and the time is scaled to the whole step by the ratio of
+    (query, key) pairs x heads, the oracle's unit of work.  Repeated until
+    about budget_s of wall time (at least once); the page copy to the host is
+    not timed."""
     import oracle
-    from chunked_prefill_mixed_hybrid_amd import workload as W
+    from oracle import sample as OS
     orc = oracle.default()
-    kc0, vc0 = W.to_host_array(ds.k_cache), W.to_host_array(ds.v_cache)
-    q, key, value = (W.to_host_array(x) for x in (ds.q, ds.key, ds.value))
+    lq = np.diff(meta.cu_seqlens_q).astype(np.int64)
+    lk = meta.seqlens_k.astype(np.int64)
+    pairs = w["pairs"]
+    e = 4 if spec.dtype == "f32" else 2
+    key_bytes = spec.num_kv_heads * spec.head_dim * e
+    seg_bytes = 2 * ((lk + 15) // 16) * 16 * key_bytes
+    total_ph = float(pairs.sum()) * spec.num_heads
+    whole = float(seg_bytes.sum()) <= max_host_bytes and total_ph <= 4 * target_pairs_heads
+    sel = np.zeros(meta.total_q, np.uint8)
+    if whole:
+        segs = list(range(meta.num_seqs))
+        sel[:] = 1
+        what = "the whole step (append + every row)"
+    else:
+        rng = np.random.default_rng(7)
+        chunks = [b for b in range(meta.num_seqs) if lq[b] > 1]
+        decs = [b for b in range(meta.num_seqs) if lq[b] == 1]
+        segs, used, ph = [], 0, 0.0
+        n_rows = 0
+        for b in chunks:  # evenly spaced rows of every chunk, up to 70 % of the target
+            if used + seg_bytes[b] > max_host_bytes:
+                continue
+            r0, n = int(meta.cu_seqlens_q[b]), int(lq[b])
+            h0 = int(lk[b] - n)
+            per_row = (h0 + np.arange(n) + 1) * float(spec.num_heads)
+            take = max(1, min(n, int(0.7 * target_pairs_heads / max(1.0, per_row.mean()))))
+            rows = np.unique(np.linspace(0, n - 1, take).round().astype(np.int64))
+            sel[r0 + rows] = 1
+            ph += float(per_row[rows].sum())
+            n_rows += len(rows)
+            segs.append(b)
+            used += int(seg_bytes[b])
+        n_dec = 0
+        for b in rng.permutation(decs):  # then decodes, while pages and work allow
+            if used + seg_bytes[b] > max_host_bytes or ph >= target_pairs_heads:
+                continue
+            sel[int(meta.cu_seqlens_q[b])] = 1
+            ph += float(lk[b]) * spec.num_heads
+            segs.append(int(b))
+            used += int(seg_bytes[b])
+            n_dec += 1
+        segs.sort()
+        what = (f"{n_rows} of {int(lq[chunks].sum())} chunk rows (evenly spaced) and {n_dec} of "
+                f"{len(decs)} decode segments (seeded pick), with the append of their tokens; "
+                f"{100.0 * ph / total_ph:.2f} % of the step's (query, key) pairs x heads, "
+                f"time scaled by that ratio")
+    smp = OS.SampledStep(meta, ds.q, ds.key, ds.value, ds.k_cache, ds.v_cache, segs)
+    rs = sel[smp.rows]
+    sample_ph = 0.0  # (query, key) pairs x heads of the selected rows
+    for b in segs:
+        r0, n = int(meta.cu_seqlens_q[b]), int(lq[b])
+        rows = np.flatnonzero(sel[r0:r0 + n])
+        sample_ph += float((lk[b] - n + rows + 1).sum()) * spec.num_heads
     runs, t_total = 0, 0.0
-    while t_total < budget_s and runs < 100:
-        kc, vc = kc0.copy(), vc0.copy()
+    while runs == 0 or (t_total < budget_s and runs < 100):
+        kc, vc = smp.kc.copy(), smp.vc.copy()
         t0 = time.perf_counter()
-        orc.append(key, value, meta.slot_mapping, kc, vc)
-        orc.attention(q, kc, vc, meta.cu_seqlens_q, meta.seqlens_k, meta.block_table)
+        orc.append(smp.key, smp.value, smp.slot_mapping, kc, vc)
+        orc.attention(smp.q, kc, vc, smp.cu, smp.sk, smp.block_table, row_select=None if whole else rs)
         t_total += time.perf_counter() - t0
         runs += 1
-    return {"value": round(1e6 * t_total / runs, 1), "unit": "us/step",
+    per_run = t_total / runs
+    return {"value": round(1e6 * per_run * total_ph / sample_ph, 1), "unit": "us/step",
             "cores": orc.num_threads(), "kind": "oracle",
-            "sample": f"the whole step (append + every row), {runs} run(s), fp64 oracle"}
+            "sample": f"{what}; fp64 oracle, {runs} run(s) of {per_run:.2f} s",
+            "host_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+            "measured_s": round(t_total, 2)}
+
+
+class Runner:
+    """One workload resident on the device, and the calls that time it."""
+
+    def __init__(self, config, seed, launch, entry, stream):
+        import torch
+        from chunked_prefill_mixed_hybrid_amd import binding as B
+        from chunked_prefill_mixed_hybrid_amd import workload as W
+        self.B, self.torch = B, torch
+        self.spec, self.meta = W.make_step(config, seed)
+        self.ds = W.device_values(self.spec, self.meta, seed=seed)
+        self.out = torch.empty_like(self.ds.q)
+        m = self.meta
+        self.ws = B.alloc_workspace(m.num_seqs, m.total_q, m.max_seqlen_k, self.spec.num_heads,
+                                    self.spec.head_dim)
+        self.launch, self.entry, self.stream = launch, entry, stream
+        self.one_call = entry == "step" and launch == "fused"
+
+    def attention(self):
+        B, ds, m = self.B, self.ds, self.meta
+        if self.launch == "fused":
+            B.hybrid_attn_fwd(ds.q, ds.k_cache, ds.v_cache, ds.cu_seqlens_q, ds.seqlens_k,
+                              ds.block_table, m.max_seqlen_q, m.max_seqlen_k, out=self.out,
+                              workspace=self.ws, stream=self.stream)
+        else:
+            B.hybrid_attn_fwd_two_launch(ds.q, ds.k_cache, ds.v_cache, ds.cu_seqlens_q,
+                                         ds.seqlens_k, ds.block_table, m.max_seqlen_q,
+                                         m.max_seqlen_k, out=self.out, workspace=self.ws,
+                                         two_streams=self.launch == "two-streams",
+                                         stream=self.stream)
+
+    def append(self):
+        ds = self.ds
+        self.B.paged_kv_append(ds.key, ds.value, ds.slot_mapping, ds.k_cache, ds.v_cache,
+                               stream=self.stream)
+
+    def step(self):
+        B, ds, m = self.B, self.ds, self.meta
+        if self.one_call:
+            B.hybrid_step_fwd(ds.key, ds.value, ds.slot_mapping, ds.q, ds.k_cache, ds.v_cache,
+                              ds.cu_seqlens_q, ds.seqlens_k, ds.block_table, m.max_seqlen_q,
+                              m.max_seqlen_k, out=self.out, workspace=self.ws, stream=self.stream)
+            return
+        self.append()
+        self.attention()
+
+    def free(self):
+        del self.ds, self.out, self.ws
+        import gc
+        gc.collect()
+        self.torch.cuda.empty_cache()
+
+
+def timed_steps(r: Runner, steps, flush_buf):
+    """Per-step durations (ms, HIP events on r.stream) of `steps` steps, each
+    preceded by a write of flush_buf when it is given; and the wall time of
+    the whole loop, bracketed by device synchronisation."""
+    torch = r.torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        if flush_buf is not None:
+            with torch.cuda.stream(r.stream):
+                flush_buf.fill_(1)
+        e0.record(r.stream)
+        r.step()
+        e1.record(r.stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return np.array([e0.elapsed_time(e1) for e0, e1 in ev]), wall
+
+
+def timed_calls(r: Runner, steps, flush_buf):
+    """Durations (ms) of the append and of the attention call, as two
+    separate calls per step (each step preceded by the flush when given)."""
+    torch = r.torch
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+    for e0, e1, e2 in ev:
+        if flush_buf is not None:
+            with torch.cuda.stream(r.stream):
+                flush_buf.fill_(1)
+        e0.record(r.stream)
+        r.append()
+        e1.record(r.stream)
+        r.attention()
+        e2.record(r.stream)
+    torch.cuda.synchronize()
+    return (np.array([e0.elapsed_time(e1) for e0, e1, _ in ev]),
+            np.array([e1.elapsed_time(e2) for _, e1, e2 in ev]))
+
+
+def percentiles(ms):
+    """p10 / p50 / p90 of per-step durations given in ms, in us."""
+    return {f"p{q}": round(float(np.percentile(ms, q)) * 1e3, 2) for q in (10, 50, 90)}
+
+
+def measure(r: Runner, steps, warmup, flush_buf):
+    torch = r.torch
+    with torch.cuda.stream(r.stream):
+        for _ in range(warmup):
+            r.step()
+    torch.cuda.synchronize()
+    cold_ms, cold_wall = timed_steps(r, steps, flush_buf)
+    warm_ms, warm_wall = timed_steps(r, steps, None)
+    append_ms, attn_ms = timed_calls(r, steps, flush_buf)
+    w = algorithmic_work(r.meta, r.spec)
+    roof_us, bound = step_roofline_us(w, r.spec)
+    cold_us = float(np.median(cold_ms)) * 1e3
+    return {"w": w, "roof_us": roof_us, "bound": bound, "cold_ms": cold_ms, "cold_us": cold_us,
+            "cold_wall": cold_wall, "warm_ms": warm_ms, "warm_wall": warm_wall,
+            "append_ms": append_ms, "attn_ms": attn_ms}
+
+
+def summary(r: Runner, m) -> dict:
+    """Per-workload figures (the extra workloads' entry of the JSON line)."""
+    attn_us = float(np.mean(m["attn_ms"])) * 1e3
+    return {"cold_us_per_step": round(m["cold_us"], 2),
+            "warm_us_per_step": round(1e3 * float(np.median(m["warm_ms"])), 2),
+            "step_roofline_us": round(m["roof_us"], 2), "bound": m["bound"],
+            "frac_step_roofline": round(m["roof_us"] / m["cold_us"], 4),
+            "attn_us": round(attn_us, 2),
+            "append_us": round(float(np.mean(m["append_ms"])) * 1e3, 2)}
 
 
 def main():
+    from chunked_prefill_mixed_hybrid_amd import workload as W
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="4", choices=list(W.CONFIGS))
+    ap.add_argument("--extra", default="1,2,3,5a,5b",
+                    help="other workloads measured after the headline one (comma list, '' for none)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold-steps", type=int, default=20,
-                    help="extra steps each preceded by a 1 GiB cache-flush write")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the 1 GiB cache-flush write before each timed step")
     ap.add_argument("--launch", default="fused", choices=["fused", "serial", "two-streams"],
                     help="fused: hybrid_attn_fwd; serial / two-streams: the two-launch baseline")
     ap.add_argument("--entry", default="step", choices=["step", "calls"],
@@ -119,132 +331,43 @@ def main():
 
     import torch
     from chunked_prefill_mixed_hybrid_amd import binding as B
-    from chunked_prefill_mixed_hybrid_amd import workload as W
 
     B.load()  # fail loudly if the HIP library is missing
     torch.cuda.set_device(0)
-    spec, meta = W.make_step(args.config, args.seed)
-    ds = W.device_values(spec, meta, seed=args.seed)
-    out = torch.empty_like(ds.q)
-    ws = B.alloc_workspace(meta.num_seqs, meta.total_q, meta.max_seqlen_k, spec.num_heads,
-                           spec.head_dim)
     stream = torch.cuda.Stream()
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush_buf = None if args.no_flush else torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
 
-    def attention():
-        if args.launch == "fused":
-            B.hybrid_attn_fwd(ds.q, ds.k_cache, ds.v_cache, ds.cu_seqlens_q, ds.seqlens_k,
-                              ds.block_table, meta.max_seqlen_q, meta.max_seqlen_k, out=out,
-                              workspace=ws, stream=stream)
-        else:
-            B.hybrid_attn_fwd_two_launch(ds.q, ds.k_cache, ds.v_cache, ds.cu_seqlens_q,
-                                         ds.seqlens_k, ds.block_table, meta.max_seqlen_q,
-                                         meta.max_seqlen_k, out=out, workspace=ws,
-                                         two_streams=args.launch == "two-streams", stream=stream)
-
-    one_call = args.entry == "step" and args.launch == "fused"
-
-    def step():
-        if one_call:
-            B.hybrid_step_fwd(ds.key, ds.value, ds.slot_mapping, ds.q, ds.k_cache, ds.v_cache,
-                              ds.cu_seqlens_q, ds.seqlens_k, ds.block_table, meta.max_seqlen_q,
-                              meta.max_seqlen_k, out=out, workspace=ws, stream=stream)
-            return
-        B.paged_kv_append(ds.key, ds.value, ds.slot_mapping, ds.k_cache, ds.v_cache, stream=stream)
-        attention()
-
-    with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            step()
-    torch.cuda.synchronize()
-
-    # timed region: exactly K steps back to back on one stream, nothing else enqueued
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    t_start.record(stream)
-    for _ in range(args.steps):
-        step()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = t_start.elapsed_time(t_end)
-
-    # the timed call on its own (HIP events on the stream the kernels run on)
-    call_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-    for e0, e1 in call_ev:
-        e0.record(stream)
-        step()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    call_ms = np.array([e0.elapsed_time(e1) for e0, e1 in call_ev])
-
-    # the append and the attention call separately (reference), a further pass
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for e0, e1, e2 in ev:
-        e0.record(stream)
-        B.paged_kv_append(ds.key, ds.value, ds.slot_mapping, ds.k_cache, ds.v_cache, stream=stream)
-        e1.record(stream)
-        attention()
-        e2.record(stream)
-    torch.cuda.synchronize()
-    attn_ms = np.array([e1.elapsed_time(e2) for _, e1, e2 in ev])
-    append_ms = np.array([e0.elapsed_time(e1) for e0, e1, _ in ev])
-    step_ms = np.array([e0.elapsed_time(e2) for e0, _, e2 in ev])
-
-    # cold steps: a 1 GiB write before each step evicts L2 and the 256 MB MALL
-    cold = []
-    for _ in range(args.cold_steps):
-        with torch.cuda.stream(stream):
-            flush_buf.fill_(1)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        cold.append(e0.elapsed_time(e1))
-
-    if args.calibrate_copy:  # a copy of known size: reads 1 GiB, writes 1 GiB
-        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    w = algorithmic_work(meta, spec)
-    us_step = 1e6 * wall / args.steps
+    r = Runner(args.config, args.seed, args.launch, args.entry, stream)
+    spec, meta = r.spec, r.meta
+    print(f"[bench] {spec.name}: {meta.num_seqs} segments, {meta.total_q} rows", file=sys.stderr,
+          flush=True)
+    m = measure(r, args.steps, args.warmup, flush_buf)
+    w = m["w"]
+    us_step = m["cold_us"]
     peak_tf = PEAK_MFMA_TFLOPS[spec.dtype]
-    t_mfma_us = w["flops"] / (peak_tf * 1e12) * 1e6
-    t_hbm_us = w["step_bytes"] / (PEAK_HBM_GBS * 1e9) * 1e6
-    roof_us = max(t_mfma_us, t_hbm_us)
-    attn_us = float(np.mean(attn_ms)) * 1e3
-    # the roofline unit: the whole step call (append + attention) with the step's
-    # bytes, or the attention call with its own bytes when the two are separate
-    unit_us = float(np.mean(call_ms)) * 1e3 if one_call else attn_us
-    unit_bytes = w["step_bytes"] if one_call else w["attn_bytes"]
-    attn_bound = "hbm" if unit_bytes / (PEAK_HBM_GBS * 1e9) >= w["flops"] / (peak_tf * 1e12) else "mfma"
-    if attn_bound == "hbm":
-        achieved = unit_bytes / (unit_us * 1e-6) / 1e9
+
+    # roofline of the attention call (planner, attn_kernel, combine): its own
+    # algorithmic bytes, or FLOPs when those bound it, over its mean duration
+    attn_us = float(np.mean(m["attn_ms"])) * 1e3
+    t_attn_hbm = w["attn_bytes"] / (PEAK_HBM_GBS * 1e9)
+    t_attn_mfma = w["flops"] / (peak_tf * 1e12)
+    if t_attn_hbm >= t_attn_mfma:
+        achieved = w["attn_bytes"] / (attn_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
     else:
-        achieved = w["flops"] / (unit_us * 1e-6) / 1e12
+        achieved = w["flops"] / (attn_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_tf,
                 "unit": "TFLOP/s", "frac": round(achieved / peak_tf, 4), "traffic": None}
-    if one_call:
-        roof["kernel"] = ("hybrid_step_fwd (append + planner in one launch, attn_kernel, combine_kernel, "
-                          "back to back)")
-    elif args.launch == "fused":
+    if args.launch == "fused":
         roof["kernel"] = "hybrid_attn_fwd (plan_kernel + attn_kernel + combine_kernel, back to back)"
+        roof["traffic"] = profiled_traffic(spec.name)
     else:
         roof["kernel"] = (f"hybrid_attn_fwd_two_launch ({args.launch}: plan, chunk launch, decode launch, "
                           "combine)")
-    roof["avg_us"] = round(unit_us, 2)
-    roof["traffic"] = profiled_traffic(spec.name, "step" if one_call else "attn") \
-        if args.launch == "fused" else None
+    roof["avg_us"] = round(attn_us, 2)
+    roof["algorithmic_bytes"] = w["attn_bytes"]
+    roof["flush"] = not args.no_flush
 
     result = {
         "metric": METRIC, "value": round(us_step, 2), "unit": "us/step", "n_gpus": 1,
@@ -256,28 +379,44 @@ def main():
                    "head_dim": spec.head_dim, "page_size": meta.page_size,
                    "max_seqlen_q": meta.max_seqlen_q, "max_seqlen_k": meta.max_seqlen_k,
                    "seed": args.seed, "launch": args.launch,
-                   "entry": "hybrid_step_fwd" if one_call else "paged_kv_append + attention"},
-        "gpu_us_per_step": round(1e3 * gpu_ms / args.steps, 2),
+                   "entry": "hybrid_step_fwd" if r.one_call else "paged_kv_append + attention",
+                   "timing": ("median of per-step HIP events, each step after a 1 GiB cache flush"
+                              if flush_buf is not None else "median of per-step HIP events, no flush")},
+        "timed_region_s": round(m["cold_wall"], 4),
+        "warm_us_per_step": round(1e6 * m["warm_wall"] / args.steps, 2),
         "tflops": round(w["flops"] / (us_step * 1e-6) / 1e12, 2),
         "kv_gbps": round(w["kv_bytes"] / (us_step * 1e-6) / 1e9, 1),
         "step_gbps": round(w["step_bytes"] / (us_step * 1e-6) / 1e9, 1),
-        "step_roofline_us": round(roof_us, 2),
-        "frac_step_roofline": round(roof_us / us_step, 4),
-        "append_us": round(float(np.mean(append_ms)) * 1e3, 2),
+        "step_roofline_us": round(m["roof_us"], 2),
+        "step_roofline_bound": m["bound"],
+        "frac_step_roofline": round(m["roof_us"] / us_step, 4),
+        "frac_step_roofline_warm": round(m["roof_us"] / (1e6 * m["warm_wall"] / args.steps), 4),
+        "append_us": round(float(np.mean(m["append_ms"])) * 1e3, 2),
         "attn_us": round(attn_us, 2),
-        "cold_us_per_step": round(float(np.median(cold)) * 1e3, 2) if cold else None,
-        "step_us_percentiles": percentiles(call_ms if one_call else step_ms),
-        "cold_us_percentiles": percentiles(np.array(cold)) if cold else None,
+        "step_us_percentiles": percentiles(m["cold_ms"]),
+        "warm_us_percentiles": percentiles(m["warm_ms"]),
         "roofline": roof,
     }
+    if args.calibrate_copy:  # a copy of known size: reads 1 GiB, writes 1 GiB
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(ds, spec, meta)
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(r.ds, spec, meta, w)
+    r.free()
+    extras = {}
+    for c in [c for c in args.extra.split(",") if c and c != args.config]:
+        rx = Runner(c, args.seed, args.launch, args.entry, stream)
+        print(f"[bench] extra workload {rx.spec.name}", file=sys.stderr, flush=True)
+        extras[rx.spec.name] = summary(rx, measure(rx, args.steps, args.warmup, flush_buf))
+        rx.free()
+    if extras:
+        result["workloads"] = extras
     print(json.dumps(result), flush=True)
-
-
-def percentiles(ms):
-    """p10 / p50 / p90 of per-step durations given in ms, in us."""
-    return {f"p{q}": round(float(np.percentile(ms, q)) * 1e3, 2) for q in (10, 50, 90)}
 
 
 if __name__ == "__main__":

@@ -8,7 +8,6 @@ library raises instead of falling back to anything else.
 from __future__ import annotations
 
 import ctypes
-import math
 from pathlib import Path
 
 LIB_PATH = Path(__file__).resolve().parent / "libhybridattn.so"
@@ -95,6 +94,11 @@ def _dev(t, name, dtype=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _scale(sm_scale) -> float:
+    """sm_scale as passed to the library: 0 asks the library for its default."""
+    return 0.0 if sm_scale is None else float(sm_scale)
+
+
 def _stream(stream):
     import torch
     if stream is None:
@@ -165,7 +169,7 @@ def hybrid_step_fwd(key, value, slot_mapping, q, k_cache, v_cache, cu_seqlens_q,
         out = torch.empty_like(q)
     if workspace is None:
         workspace = alloc_workspace(b, t, max_seqlen_k, hq, d, device=q.device)
-    scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(d)
+    scale = _scale(sm_scale)
     dt = q.dtype
     st = load().hybrid_step_fwd(
         _dev(key, "key", dt), _dev(value, "value", dt),
@@ -196,7 +200,7 @@ def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
         out = torch.empty_like(q)
     if workspace is None:
         workspace = alloc_workspace(b, t, max_seqlen_k, hq, d, device=q.device)
-    scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(d)
+    scale = _scale(sm_scale)
     dt = q.dtype
     st = load().varlen_attn_fwd(
         _dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt),
@@ -222,7 +226,7 @@ def _attn(fn, q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table, max_seq
         out = torch.empty_like(q)
     if workspace is None:
         workspace = alloc_workspace(b, t, max_seqlen_k, hq, d, device=q.device)
-    scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(d)
+    scale = _scale(sm_scale)
     dt = q.dtype
     st = getattr(load(), fn)(
         _dev(q, "q", dt), _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),

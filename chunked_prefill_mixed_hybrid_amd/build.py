@@ -20,7 +20,7 @@ CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIB = PKG / "libhybridattn.so"
 SOURCES = ["api.hip", "attention.hip", "kv_append.hip"]
-HOST_SOURCES = ["scheduler.cpp"]  # host-only C++ (no device code), built with the host compiler
+HOST_SOURCES = ["scheduler.cpp", "status.cpp"]  # host-only C++ (no device code), built with the host compiler
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -15,17 +15,6 @@ bool supported_shape(int head_dim, int page_size, ha_dtype dtype) {
 
 extern "C" {
 
-const char* ha_status_string(ha_status status) {
-  switch (status) {
-    case HA_OK: return "HA_OK";
-    case HA_ERR_INVALID_ARGUMENT: return "HA_ERR_INVALID_ARGUMENT";
-    case HA_ERR_UNSUPPORTED: return "HA_ERR_UNSUPPORTED";
-    case HA_ERR_WORKSPACE_TOO_SMALL: return "HA_ERR_WORKSPACE_TOO_SMALL";
-    case HA_ERR_HIP: return "HA_ERR_HIP";
-  }
-  return "HA_ERR_UNKNOWN";
-}
-
 ha_status paged_kv_append(const void* key, const void* value, const int32_t* slot_mapping,
                           void* k_cache, void* v_cache, int32_t total_tokens,
                           int32_t num_kv_heads, int32_t head_dim, int32_t page_size,

@@ -33,6 +33,7 @@
 //         per lane, merged across the waves through LDS.  (fp32: one head per
 //         wave.)  Splits of a segment write partial (m, l, acc) rows that
 //         combine_kernel merges.
+#include <atomic>
 #include <mutex>
 
 #include "ha_common.hpp"
@@ -1849,35 +1850,41 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(MainArgs a) {
 // ==================================================================== launch
 namespace {
 
+// Per-device attributes, queried on first use.  Calls from several host
+// threads may query them at once: each writes the same value, through an
+// atomic, so the race is benign.
 struct DeviceInfo {
-  int cus = 0;
-  int slots[2][2][2] = {};  // [dtype][D == 128][split-capable] resident workgroups per CU
+  std::atomic<int> cus{0};
+  std::atomic<int> slots[2][2][2] = {};  // [dtype][D == 128][split-capable] resident workgroups per CU
 };
 
 DeviceInfo g_info[64];
 
 hipError_t occupancy(DeviceInfo& info, int dt, int di, int ds, const void* kernel, int& grid) {
-  if (info.slots[dt][di][ds] == 0) {
-    int n = 0;
+  int n = info.slots[dt][di][ds].load(std::memory_order_relaxed);
+  if (n == 0) {
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kThreads, 0);
     if (e != hipSuccess) return e;
-    info.slots[dt][di][ds] = n > 0 ? n : 1;
+    n = n > 0 ? n : 1;
+    info.slots[dt][di][ds].store(n, std::memory_order_relaxed);
   }
-  grid = info.cus * info.slots[dt][di][ds];
+  grid = info.cus.load(std::memory_order_relaxed) * n;
   return hipSuccess;
 }
 
 // Second stream and fork/join events of the two-stream baseline, per device,
-// created on first use (default priority).
+// created on first use (default priority) under the device's lock.
 struct SideStream {
   hipStream_t stream = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
-  std::mutex lock;  // the record / wait / launch sequence of one call
+  std::mutex lock;  // creation, then the record / wait / launch sequence of each call
 };
 SideStream g_side[64];
 
-hipError_t side_stream(int dev, SideStream*& out) {
+// Returns the device's side stream with its lock held by `held`.
+hipError_t side_stream(int dev, SideStream*& out, std::unique_lock<std::mutex>& held) {
   SideStream& s = g_side[dev];
+  held = std::unique_lock<std::mutex>(s.lock);
   if (!s.stream) {
     hipError_t e = hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&s.fork, hipEventDisableTiming);
@@ -1909,7 +1916,7 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
   // item per CU.  fp32 tiles leave a CU underused with one workgroup (long
   // fp32 MFMA chains): there they go up to one item per resident workgroup
   // (worked example: 238 us against 308 us with one item per CU).
-  const int split_items = sizeof(T) == 4 ? grid : info.cus;
+  const int split_items = sizeof(T) == 4 ? grid : info.cus.load(std::memory_order_relaxed);
   const bool split_ok = L.ws.chunk_slots_cap >= 2 &&
                         2LL * L.ws.tiles_cap * L.num_heads <= static_cast<long long>(split_items);
   if (split_ok) {
@@ -1917,8 +1924,9 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
     if (e != hipSuccess) return e;
   }
   SideStream* side = nullptr;
+  std::unique_lock<std::mutex> side_held;  // held until the call has enqueued its launches
   if (L.launch_mode == kLaunchTwoStreams) {
-    e = side_stream(dev, side);
+    e = side_stream(dev, side, side_held);
     if (e != hipSuccess) return e;
   }
   // workgroups per launch and how many of them start on the chunk queues
@@ -2010,7 +2018,6 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
       attn(md, grid, L.stream);
     } else {
       mc.chunk_wgs = half;
-      std::lock_guard<std::mutex> g(side->lock);
       e = hipEventRecord(side->fork, L.stream);
       if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
       if (e != hipSuccess) return e;
@@ -2036,9 +2043,11 @@ hipError_t launch_attention(const AttnLaunch& L) {
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   DeviceInfo& info = g_info[dev];
-  if (info.cus == 0) {
-    e = hipDeviceGetAttribute(&info.cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (info.cus.load(std::memory_order_relaxed) == 0) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
+    info.cus.store(cus, std::memory_order_relaxed);
   }
   if (L.cu_seqlens_k) {
     if (L.dtype == 1) {

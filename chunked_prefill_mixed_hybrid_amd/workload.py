@@ -76,12 +76,21 @@ def _decodes(rng, n, lo, hi):
     return [(1, int(h) + 1) for h in hist]
 
 
-def config_spec(config: int, seed: int = 0) -> tuple:
-    """(StepSpec, rng) for workload configs 1..5 (5 = the budget-2048 step).
+CONFIGS = ("1", "2", "3", "4", "5", "5a", "5b")
+
+
+def config_spec(config, seed: int = 0) -> tuple:
+    """(StepSpec, rng) for workload configs 1..5 (5 or "5a" = the budget-2048
+    step; "5b" = the 10000-token prompt of the chunk-equivalence run prefilled
+    in one step, 64 heads x 128, bf16).
 
     The returned rng has drawn the decode histories and is then used for the
     block-id permutation, so the whole step follows from (config, seed)."""
     rng = np.random.default_rng(seed)
+    config = str(config)
+    if config == "5b":
+        return StepSpec("full_prefill_10000_64x128", [(10000, 10000)], 64, 64, 128, BF16), rng
+    config = 5 if config == "5a" else int(config)
     if config == 1:
         segs = [(1, 121), (1, 46), (1808, 10000)]
         return StepSpec("worked_example", segs, 2, 2, 64, F32), rng
@@ -149,7 +158,7 @@ def build_meta(spec: StepSpec, rng: np.random.Generator) -> StepMeta:
                     int(lks.max()) if len(lks) else 0, poison)
 
 
-def make_step(config: int, seed: int = 0):
+def make_step(config, seed: int = 0):
     spec, rng = config_spec(config, seed)
     return spec, build_meta(spec, rng)
 

@@ -28,6 +28,10 @@
  *     library keeps no pointer after a call returns, allocates no device
  *     memory, and never synchronises: work is enqueued on `stream` (a
  *     hipStream_t; NULL = the default stream) and the call returns at once.
+ *   - Calls from several host threads may run at once (each with its own
+ *     workspace): the per-device attribute cache behind the launches is
+ *     written through atomics, and the two-stream baseline creates its stream
+ *     under a per-device lock.
  *   - No exception crosses the ABI.  Host-checkable argument problems are
  *     reported before anything is enqueued.  HA_ERR_HIP reports a failed
  *     launch (hipGetLastError after the launch).

@@ -56,7 +56,9 @@ class Oracle:
     """One loaded copy of the oracle library (the real one, or a test mutant)."""
 
     def __init__(self, path: Path | str | None = None):
-        path = Path(path) if path else HERE / LIB_NAME
+        # ORACLE_LIB names another build of oracle.c to load by default (the
+        # sanitizer test runs the pins against an ASan/UBSan build this way)
+        path = Path(path or os.environ.get("ORACLE_LIB") or HERE / LIB_NAME)
         if not path.exists():
             build(out=path)
         self.path = path

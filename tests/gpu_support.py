@@ -9,6 +9,7 @@ import numpy as np
 from chunked_prefill_mixed_hybrid_amd import binding as B
 from chunked_prefill_mixed_hybrid_amd import workload as W
 import oracle as O
+from oracle import sample as OS
 
 # Tolerances: fp32 max |err| <= 1e-4; bf16 max |err| <= 2e-2 AND
 # ||err||_2 / ||ref||_2 <= 1e-2 (both must hold); any NaN/Inf fails.
@@ -111,53 +112,7 @@ def oracle_full(ds: W.DeviceStep, kc_host, vc_host, row_select=None):
     return out, kc, vc
 
 
-class SampledStep:
-    """Pages, rows and metadata of a few segments of a big step, copied to the
-    host BEFORE the GPU append, with block ids renumbered compactly, so the
-    oracle can check those segments (and their append) on its own."""
-
-    def __init__(self, ds: W.DeviceStep, segs):
-        import torch
-        m = ds.meta
-        p = m.page_size
-        self.segs = list(segs)
-        pages, rows, lqs, lks = [], [], [], []
-        for b in self.segs:
-            lk = int(m.seqlens_k[b])
-            r0, r1 = int(m.cu_seqlens_q[b]), int(m.cu_seqlens_q[b + 1])
-            n = (lk + p - 1) // p
-            pages.append(m.block_table[b, :n].astype(np.int64))
-            rows.append(np.arange(r0, r1))
-            lqs.append(r1 - r0)
-            lks.append(lk)
-        allp = np.concatenate(pages)
-        self.pages = allp
-        self.rows = np.concatenate(rows)
-        remap = {int(pg): i for i, pg in enumerate(allp)}
-        mb = max(len(x) for x in pages)
-        bt = np.full((len(self.segs), mb), -1, np.int32)
-        off = 0
-        for i, x in enumerate(pages):
-            bt[i, :len(x)] = np.arange(off, off + len(x))
-            off += len(x)
-        self.block_table = bt
-        self.cu = np.concatenate([[0], np.cumsum(lqs)]).astype(np.int32)
-        self.sk = np.array(lks, np.int32)
-        slots = m.slot_mapping[self.rows].astype(np.int64)
-        self.slot_mapping = np.array([remap[int(s) // p] * p + int(s) % p for s in slots], np.int32)
-        idx = torch.from_numpy(allp).to(ds.k_cache.device)
-        self.kc = W.to_host_array(ds.k_cache.index_select(0, idx))
-        self.vc = W.to_host_array(ds.v_cache.index_select(0, idx))
-        ridx = torch.from_numpy(self.rows).to(ds.q.device)
-        self.q = W.to_host_array(ds.q.index_select(0, ridx))
-        self.key = W.to_host_array(ds.key.index_select(0, ridx))
-        self.value = W.to_host_array(ds.value.index_select(0, ridx))
-        self.page_idx = idx
-
-    def oracle(self, row_select=None):
-        orc = O.default()
-        kc, vc = self.kc.copy(), self.vc.copy()
-        orc.append(self.key, self.value, self.slot_mapping, kc, vc)
-        out = orc.attention(self.q, kc, vc, self.cu, self.sk, self.block_table,
-                            row_select=row_select)
-        return out, kc, vc
+def sampled_step(ds: W.DeviceStep, segs) -> OS.SampledStep:
+    """Host copies of the pages, rows and metadata of segments `segs` of a
+    device step (taken before its append), for the oracle."""
+    return OS.SampledStep(ds.meta, ds.q, ds.key, ds.value, ds.k_cache, ds.v_cache, segs)
