@@ -97,7 +97,7 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(ds, spec, meta, w, budget_s=15.0, max_host_bytes=6 << 30, target_pairs_heads=2.5e9):
+def cpu_baseline(ds, spec, meta, w, budget_s=15.0, max_host_bytes=6 << 30, target_pairs_heads=1e9):
     """The oracle (as it stands) on the host cores.  Steps whose pages fit
     max_host_bytes and whose work is small run whole (append + every row);
     bigger ones run a bounded sample -- evenly spaced rows of the chunk
