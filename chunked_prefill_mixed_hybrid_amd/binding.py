@@ -16,7 +16,8 @@ HA_OK, HA_ERR_INVALID_ARGUMENT, HA_ERR_UNSUPPORTED, HA_ERR_WORKSPACE_TOO_SMALL, 
 HA_DTYPE_F32, HA_DTYPE_BF16 = 0, 1
 
 EXPORTED = ("ha_status_string", "paged_kv_append", "hybrid_attn_workspace_size", "hybrid_attn_fwd",
-            "hybrid_attn_fwd_two_launch", "varlen_attn_fwd", "hybrid_step_fwd")
+            "hybrid_attn_fwd_two_launch", "varlen_attn_fwd", "hybrid_step_fwd",
+            "hybrid_step_fwd_noalloc")
 
 
 class HybridAttnError(RuntimeError):
@@ -61,6 +62,9 @@ def load(path: Path | str | None = None) -> ctypes.CDLL:
     lib.hybrid_step_fwd.argtypes = ([vp, vp, i32p, vp, vp, vp, i32p, i32p, i32p, vp] + [i32] * 10 +
                                     [ctypes.c_float, ctypes.c_int, vp, ctypes.c_size_t, vp])
     lib.hybrid_step_fwd.restype = ctypes.c_int
+    lib.hybrid_step_fwd_noalloc.argtypes = ([vp, vp, i32p, vp, vp, vp, i32p, i32p, i32p, vp] +
+                                            [i32] * 10 + [ctypes.c_float, ctypes.c_int, vp])
+    lib.hybrid_step_fwd_noalloc.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -181,6 +185,33 @@ def hybrid_step_fwd(key, value, slot_mapping, q, k_cache, v_cache, cu_seqlens_q,
         scale, _dtype_code(q), _dev(workspace, "workspace", torch.uint8), workspace.numel(),
         _stream(stream))
     _check("hybrid_step_fwd", st)
+    return out
+
+
+def hybrid_step_fwd_noalloc(key, value, slot_mapping, q, k_cache, v_cache, cu_seqlens_q,
+                            seqlens_k, block_table, max_seqlen_q, max_seqlen_k, out,
+                            sm_scale=None, stream=None):
+    """hybrid_step_fwd with the library's own device scratch array as its
+    workspace: the call allocates no device memory (`out` is the caller's)."""
+    import torch
+    t, hq, d = q.shape
+    nb, p, hkv, d2 = k_cache.shape
+    if d2 != d or v_cache.shape != k_cache.shape or key.shape != (t, hkv, d) or value.shape != key.shape:
+        raise ValueError("hybrid_step_fwd_noalloc: shape mismatch")
+    b = seqlens_k.shape[0]
+    if (cu_seqlens_q.shape != (b + 1,) or block_table.dim() != 2 or block_table.shape[0] != b
+            or slot_mapping.shape != (t,) or out.shape != q.shape):
+        raise ValueError("hybrid_step_fwd_noalloc: metadata or output shapes")
+    dt = q.dtype
+    st = load().hybrid_step_fwd_noalloc(
+        _dev(key, "key", dt), _dev(value, "value", dt),
+        _dev(slot_mapping, "slot_mapping", torch.int32), _dev(q, "q", dt),
+        _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(seqlens_k, "seqlens_k", torch.int32),
+        _dev(block_table, "block_table", torch.int32), _dev(out, "out", dt),
+        b, t, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, p, nb, block_table.shape[1],
+        _scale(sm_scale), _dtype_code(q), _stream(stream))
+    _check("hybrid_step_fwd_noalloc", st)
     return out
 
 

@@ -151,6 +151,35 @@ inline WsLayout ws_layout(int num_seqs, int total_q, int max_seqlen_k, int num_h
   return l;
 }
 
+// The same layout within max_bytes: the partial-slot capacities shrink until
+// the arrays fit -- decode partials first to at most half of the room left
+// after the fixed arrays, then chunk-tile partials to what remains (none when
+// fewer than 2 slots fit), then decode partials to the rest.  The planner
+// adapts: it picks decode splits whose partial slots fit parts_cap (the
+// largest split needs none) and splits chunk tiles only into slots that exist.
+// total > max_bytes only when the fixed arrays alone do not fit.
+inline WsLayout ws_layout_within(int num_seqs, int total_q, int max_seqlen_k, int num_heads,
+                                 int head_dim, size_t max_bytes) {
+  WsLayout l = ws_layout(num_seqs, total_q, max_seqlen_k, num_heads, head_dim);
+  if (l.total <= max_bytes || l.partials > max_bytes) return l;
+  const size_t part_bytes = sizeof(float) * static_cast<size_t>(num_heads) * l.part_stride;
+  const size_t slot_bytes = part_bytes * kChunkRows;
+  if (max_bytes - l.partials < 512) return l;
+  const size_t room = max_bytes - l.partials - 512;  // the two arrays' alignment pads kept aside
+  size_t parts = room / 2 / part_bytes;
+  if (parts > static_cast<size_t>(l.parts_cap)) parts = l.parts_cap;
+  size_t slots = (room - parts * part_bytes) / slot_bytes;
+  if (slots > static_cast<size_t>(l.chunk_slots_cap)) slots = l.chunk_slots_cap;
+  if (slots < 2) slots = 0;
+  parts = (room - slots * slot_bytes) / part_bytes;
+  if (parts > static_cast<size_t>(l.parts_cap)) parts = l.parts_cap;
+  l.parts_cap = static_cast<int>(parts);
+  l.chunk_slots_cap = static_cast<int>(slots);
+  l.chunk_partials = l.partials + align256(parts * part_bytes);
+  l.total = l.chunk_partials + align256(slots * slot_bytes);
+  return l;
+}
+
 // ---- launchers ---------------------------------------------------------------------
 // How the chunk role and the decode role are launched: one fused persistent
 // kernel (the product path), or -- as a comparison baseline -- two launches,

@@ -179,6 +179,40 @@ ha_status hybrid_step_fwd(const void* key, const void* value, const int32_t* slo
                           size_t workspace_bytes, void* stream);
 
 /*
+ * hybrid_step_fwd_noalloc -- hybrid_step_fwd without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); its
+ * workspace is a 64 MiB array in the library's device code, one copy per GPU,
+ * held from the library's load until the process ends.  The first call on a
+ * device looks up that array's address (hipGetSymbolAddress) with the device
+ * current.
+ *
+ * Arguments, result and errors: those of hybrid_step_fwd, minus workspace and
+ * workspace_bytes.  Steps whose workspace (hybrid_attn_workspace_size) fits in
+ * 64 MiB get byte for byte the output of hybrid_step_fwd; for bigger steps the
+ * split-KV partial-result capacities shrink to fit, the planner picks coarser
+ * splits, and the output stays within the same tolerance of the exact result.
+ * HA_ERR_WORKSPACE_TOO_SMALL: the per-segment plan arrays alone exceed the
+ * array (more than about four million segments).
+ *
+ * The array keeps the last call's contents; every call rewrites what it reads
+ * (plan, counters, partials), so contents on entry do not matter.  All calls
+ * on one GPU share the array: calls that overlap in time on that GPU (two
+ * streams, or two host threads whose streams are not ordered) race on it and
+ * must be serialised by the caller, e.g. by issuing them on one stream.
+ */
+ha_status hybrid_step_fwd_noalloc(const void* key, const void* value, const int32_t* slot_mapping,
+                                  const void* q, void* k_cache, void* v_cache,
+                                  const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                                  const int32_t* block_table, void* out, int32_t num_seqs,
+                                  int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                  int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t page_size, int32_t num_blocks,
+                                  int32_t max_blocks_per_seq, float sm_scale, ha_dtype dtype,
+                                  void* stream);
+
+/*
  * hybrid_attn_fwd_two_launch -- the same computation as hybrid_attn_fwd, but
  * with the chunk (prefill) role and the decode role in two separate kernel
  * launches instead of one fused launch: the "separate prefill and decode

@@ -76,6 +76,15 @@ def contiguous_kv(ds: W.DeviceStep, poison_rows: int = 5):
             torch.from_numpy(cu_k).to(k.device))
 
 
+def equal_device(a, b, slab=1 << 29) -> bool:
+    """Bitwise equality of two device tensors, compared in slabs of raw bytes."""
+    import torch
+    fa, fb = a.reshape(-1).view(torch.uint8), b.reshape(-1).view(torch.uint8)
+    if fa.numel() != fb.numel():
+        return False
+    return all(torch.equal(fa[s:s + slab], fb[s:s + slab]) for s in range(0, fa.numel(), slab))
+
+
 def to_f64(t) -> np.ndarray:
     return O.to_f64(W.to_host_array(t))
 

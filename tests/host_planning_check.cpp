@@ -106,6 +106,24 @@ int main() {
     }
     if (l.tile_prefix < sizeof(PlanHeader)) return fail("header overlap", b, 0, 0);
     if (l.chunk_slots_cap != 0 && l.chunk_slots_cap < 2) return fail("chunk slots", b, l.chunk_slots_cap, 0);
+    // the same step within a bounded scratch buffer: capacities only shrink,
+    // arrays stay aligned and in order, and everything fits once the fixed
+    // arrays do
+    const size_t cap_bytes = static_cast<size_t>(1 + rng() % 64) << 20;
+    const WsLayout c = ws_layout_within(b, static_cast<int>(total_q), max_k, hq, d, cap_bytes);
+    if (c.partials != l.partials) return fail("capped layout moved the fixed arrays", b, 0, 0);
+    if (c.parts_cap > l.parts_cap || c.chunk_slots_cap > l.chunk_slots_cap || c.parts_cap < 0)
+      return fail("capped capacities grew", b, c.parts_cap, c.chunk_slots_cap);
+    if (c.chunk_slots_cap != 0 && c.chunk_slots_cap < 2) return fail("capped chunk slots", b, c.chunk_slots_cap, 0);
+    if (c.chunk_partials % 256 != 0 || c.total % 256 != 0 || c.chunk_partials < c.partials)
+      return fail("capped layout alignment", b, 0, 0);
+    const size_t part_bytes = sizeof(float) * static_cast<size_t>(hq) * c.part_stride;
+    if (c.chunk_partials - c.partials < static_cast<size_t>(c.parts_cap) * part_bytes ||
+        c.total - c.chunk_partials < static_cast<size_t>(c.chunk_slots_cap) * part_bytes * kChunkRows)
+      return fail("capped arrays overlap", b, c.parts_cap, c.chunk_slots_cap);
+    if (l.total <= cap_bytes && c.total != l.total) return fail("layout capped although it fits", b, 0, 0);
+    if (l.partials + 512 <= cap_bytes && c.total > cap_bytes)
+      return fail("capped layout too big", b, static_cast<long long>(c.total), static_cast<long long>(cap_bytes));
   }
   std::printf("host planning checks passed\n");
   return 0;

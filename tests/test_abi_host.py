@@ -144,3 +144,20 @@ def test_append_argument_errors(lib):
     assert app(lib, D=80) == B.HA_ERR_UNSUPPORTED
     assert app(lib, P=8) == B.HA_ERR_UNSUPPORTED
     assert app(lib, T=0) == B.HA_OK
+
+
+def test_noalloc_step_argument_errors(lib):
+    """hybrid_step_fwd_noalloc rejects bad arguments, and steps whose plan
+    arrays alone exceed its 64 MiB scratch array, before touching the GPU."""
+    def call(**kw):
+        args = dict(key=FAKE, value=FAKE, slot=FAKE, q=FAKE, kc=FAKE, vc=FAKE, cu=FAKE, sk=FAKE,
+                    bt=FAKE, out=FAKE, B=3, T=1810, mq=1808, mk=10000, H=2, Hkv=2, D=64, P=16,
+                    NB=644, MB=625, scale=0.0, dt=B.HA_DTYPE_F32)
+        args.update(kw)
+        return lib.hybrid_step_fwd_noalloc(*args.values(), None)
+    assert call(key=None) == B.HA_ERR_INVALID_ARGUMENT
+    assert call(Hkv=3) == B.HA_ERR_INVALID_ARGUMENT
+    assert call(D=96) == B.HA_ERR_UNSUPPORTED
+    assert call(bt=None) == B.HA_ERR_INVALID_ARGUMENT
+    # 5 million segments: four int32 plan arrays of 20 MB each do not fit
+    assert call(B=5_000_000, T=5_000_000, mq=1, mk=16) == B.HA_ERR_WORKSPACE_TOO_SMALL
