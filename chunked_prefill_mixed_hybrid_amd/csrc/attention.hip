@@ -500,18 +500,18 @@ __device__ __forceinline__ int segment_row0(const MainArgs& a, int seg) {
 // memory load and nothing else: vmcnt 0, expcnt 7, lgkmcnt 15.
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-// XOR swizzle (in 16-byte chunks of 8 keys) of row d of the transposed V tile.
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
 constexpr uint32_t kBf16PairOne = 0x3f803f80u;  // (1.0, 1.0) as a bf16 pair
 
 template <typename T> struct ChunkCfg;
+// bf16: a stage holds a 64-key step of K and of V, both key-major (rows of 2D
+// bytes, no padding); two stages.
 template <> struct ChunkCfg<bf16_t> {
   template <int D> struct Sizes {
     static constexpr int BN = 64;
-    static constexpr int KROW = (D + 8) * 2;   // bytes per key row of the K tile
-    static constexpr int VROW = BN * 2;        // bytes per channel row of V^T (swizzled, no pad)
-    static constexpr int STAGE = BN * KROW + D * VROW;
-    static constexpr int BYTES = 2 * STAGE;    // double buffered
+    static constexpr int ROW = D * 2;                    // bytes per key row
+    static constexpr int POOL = BN * ROW;                // one pool's step
+    static constexpr int STAGE = 2 * POOL;               // K, then V
+    static constexpr int BYTES = 2 * STAGE;              // two stages
   };
 };
 template <> struct ChunkCfg<float> {
@@ -565,8 +565,38 @@ __device__ __forceinline__ void chunk_store_partial(const MainArgs& a, int seg, 
 }
 
 // ---------------------------------------------------------------- chunk role, bf16
+// LDS layout of a stage (row R = key of the 64-key step, 2D bytes per row):
+// the 16-byte chunks of a row are stored at swizzled positions, chunk c of
+// row R at c ^ swz(R), with one swizzle for K and one for V, chosen so that the
+// MFMA operand reads below hit distinct LDS banks:
+//   K: 8 or 16 consecutive lanes read chunk c of the rows key_perm(0..15); at
+//      D = 128 (256-byte rows, every row starting at bank 0) swz = R & 15; at
+//      D = 64 (128-byte rows, odd rows on the other half of the banks) swz =
+//      (R >> 1) & 7.
+//   V: a transposing read (ds_read_b64_tr_b16) of one 16-lane group covers 4
+//      consecutive rows and 2 adjacent chunks; swz shifts those rows' chunk
+//      pairs apart: (R & 3) << 1 at D = 128, ((R >> 1) & 1) << 1 at D = 64.
+template <int D> __device__ __forceinline__ int kswz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D> __device__ __forceinline__ int vswz(int r) {
+  return D == 128 ? ((r & 3) << 1) : (((r >> 1) & 1) << 1);
+}
+
 // kSplit: the tile is one of nsplit key ranges (else nsplit == 1, split == 0);
 // kContig: keys in a packed buffer instead of pages
+//
+// Data movement: each 64-key step of K and V goes from the pool straight into
+// an LDS stage (buffer loads with the LDS bit: lane i of a wave instruction
+// writes bytes 16 i .. 16 i + 15 of a 1 KB block, from whatever source offset
+// the lane gives, so the swizzle is applied on the source side; lanes whose
+// offset is out of range, or whose page descriptor is empty, write zeros).
+// Wave w loads the step's keys 16 w .. 16 w + 15, one page.  Two stages: the
+// next step's loads are issued as soon as the barrier closing the previous
+// step has freed its stage, and waited for (vmcnt) before the barrier closing
+// this step.  No registers hold staged data and no VALU work transposes V:
+// the P.V operand V^T (32 channels x 8 keys per lane) is read with two
+// transposing LDS reads per MFMA.
 template <int D, bool kSplit, bool kContig, bool kQWait>
 __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, int split, int nsplit,
                                 unsigned char* smem) {
@@ -576,11 +606,10 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, int
   }
   using Cfg = ChunkCfg<bf16_t>::Sizes<D>;
   constexpr int BN = Cfg::BN, NKB = BN / 32, KS = D / 16, NM = D / 32;
-  constexpr int KROW = Cfg::KROW, VROW = Cfg::VROW, STAGE = Cfg::STAGE;
-  constexpr int CPR = D * 2 / 16;              // 16-byte chunks per key row
-  constexpr int KLOADS = BN * CPR / kThreads;  // K chunks per thread per tile
-  constexpr int VKG = BN * CPR / kThreads;     // keys per thread in the V transpose
-  static_assert(KLOADS * kThreads == BN * CPR, "tile load must divide evenly");
+  constexpr int ROW = Cfg::ROW, POOL = Cfg::POOL, STAGE = Cfg::STAGE;
+  constexpr int CPR = D / 8;          // 16-byte chunks per key row
+  constexpr int RPI = kWave / CPR;    // rows per wave load instruction (1 KB)
+  constexpr int IPW = kPage / RPI;    // load instructions per wave, per pool and step
 
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int qc = lane & 31, g = lane >> 5;
@@ -605,9 +634,8 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, int
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = ok ? ld16(qp + s * 16) : u32x4_t{0, 0, 0, 0};
   }
-  // kQWait: wait for the Q loads here, once per tile.  Left pending into the
-  // key loop, they make the compiler wait for every outstanding global load
-  // (the next tiles' K/V prefetch included) before each step's first MFMA.
+  // kQWait: wait for the Q loads here, once per tile, instead of at the first
+  // MFMA of every key step (where the wait would also cover the step's loads)
   if constexpr (kQWait) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   f32x16_t acc[NM];
@@ -615,102 +643,56 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, int
   for (int m = 0; m < NM; ++m) acc[m] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Tile loads.  Every 16-byte load of a tile reads from one page that is the
-  // same for the whole wave (K load `it`: page (it*256 + 64w) / (16*CPR) of the
-  // tile; V: page w), so page ids are scalar block-table reads and the gathers
-  // are buffer loads with a 32-bit lane offset.  Keys at or past kb1 read as
-  // zero (offset out of range, or an empty descriptor for whole pages).
   const_i32_t* btrow = (const_i32_t*)(a.bt) + static_cast<size_t>(seg) * a.max_blocks;
   const int last_page = (max(kb1, 1) - 1) >> 4;
   const uint32_t slot_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 2;
   const uint32_t page_bytes = slot_bytes * kPage;
   const uint32_t head_off = static_cast<uint32_t>(kvh) * D * 2;
   const int krow0 = segment_row0<kContig>(a, seg);  // first key row (contiguous K/V)
-  const int vc_ = tid % CPR, vkg = tid / CPR;  // V transpose: chunk and key group of this thread
-  u32x4_t kreg[KLOADS], vreg[VKG];
-  // page ids of a tile (scalar loads); -1 past kend or outside the pool
-  auto tile_ids = [&](int k0, int (&ids)[4]) {
+  // this lane's part of every load: row (within its wave's page) and chunk
+  const int lrow = lane / CPR, lpos = lane % CPR;
+  // loads of the step at key k0 into stage st; id: the block id of this wave's page
+  auto issue_step = [&](int k0, int id, unsigned char* st) {
+    const int range = id >= 0 ? static_cast<int>(page_bytes) : 0;
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(page_base<kContig>(a.kc, id, slot_bytes, page_bytes), 0,
+                                                      range, kRawBufferWord3);
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc(page_base<kContig>(a.vc, id, slot_bytes, page_bytes), 0,
+                                                      range, kRawBufferWord3);
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp)
-      ids[pp] = segment_page<kContig>(btrow, krow0, (k0 >> 4) + pp, last_page, a.num_blocks);
-  };
-  auto issue_tile = [&](int k0, const int (&ids)[4]) {
-    auto rsrc = [&](const void* pool, int pidx) {  // pidx uniform: select, no indexed array
-      const int id = pidx == 0 ? ids[0] : pidx == 1 ? ids[1] : pidx == 2 ? ids[2] : ids[3];
-      return __builtin_amdgcn_make_buffer_rsrc(page_base<kContig>(pool, id, slot_bytes, page_bytes), 0,
-                                               id < 0 ? 0 : static_cast<int>(page_bytes),
-                                               kRawBufferWord3);
-    };
-#pragma unroll
-    for (int it = 0; it < KLOADS; ++it) {
-      const int key = (it * kThreads + tid) / CPR;
-      const uint32_t off = (k0 + key < kb1)
-                               ? (key & 15) * slot_bytes + head_off + (tid % CPR) * 16
-                               : kOffsetOutOfRange;
-      const auto rs = rsrc(a.kc, (it * kThreads + w * kWave) / (16 * CPR));
-      kreg[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-    }
-    const auto rs = rsrc(a.vc, w);
-#pragma unroll
-    for (int t = 0; t < VKG; ++t) {
-      const int key = vkg * VKG + t;
-      const uint32_t off = (k0 + key < kb1)
-                               ? (key & 15) * slot_bytes + head_off + vc_ * 16
-                               : kOffsetOutOfRange;
-      vreg[t] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    for (int j = 0; j < IPW; ++j) {
+      const int r = RPI * j + lrow;  // key within the page (= row within the wave's 16)
+      const int row = 16 * w + r;    // row within the step
+      const bool in = k0 + row < kb1;
+      const uint32_t base = static_cast<uint32_t>(r) * slot_bytes + head_off;
+      const uint32_t ok_ = in ? base + static_cast<uint32_t>(lpos ^ kswz<D>(row)) * 16 : kOffsetOutOfRange;
+      const uint32_t ov_ = in ? base + static_cast<uint32_t>(lpos ^ vswz<D>(row)) * 16 : kOffsetOutOfRange;
+      unsigned char* dk = st + (16 * w + RPI * j) * ROW;
+      load_lds16(rk, dk, ok_);
+      load_lds16(rv, dk + POOL, ov_);
     }
   };
-  // Registers -> one LDS stage: K natural Ks[key][d]; V transposed Vt[d][key]
-  // with 128-byte rows whose 16-byte chunks (8 keys) are XOR-swizzled by
-  // vt_swz(d): the transposed writes (16 lanes on rows 8 apart) and the MFMA
-  // operand reads (32 consecutive rows) then spread over all LDS banks.
-  auto store_tile = [&](unsigned char* st) {
-#pragma unroll
-    for (int it = 0; it < KLOADS; ++it) {
-      const int idx = it * kThreads + tid;
-      st16(st + (idx / CPR) * KROW + (idx % CPR) * 16, kreg[it]);
-    }
-    unsigned char* vt = st + BN * KROW;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint32_t hv[VKG];
-#pragma unroll
-      for (int t = 0; t < VKG; ++t) {
-        const uint32_t word = vreg[t][e >> 1];
-        hv[t] = (e & 1) ? (word >> 16) : (word & 0xffffu);
-      }
-      const int d = vc_ * 8 + e;
-      unsigned char* dst = vt + d * VROW + (((vkg * VKG) >> 3) ^ vt_swz(d)) * 16 + ((vkg * VKG) & 7) * 2;
-      if constexpr (VKG == 4) {
-        st8(dst, u32x2_t{hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)});
-      } else {
-        static_assert(VKG == 2, "V transpose handles 2 or 4 keys per thread");
-        *reinterpret_cast<uint32_t*>(dst) = hv[0] | (hv[1] << 16);
-      }
-    }
+  auto page_id = [&](int k0) {  // scalar load; -1 past the range or outside the pool
+    return segment_page<kContig>(btrow, krow0, (k0 >> 4) + w, last_page, a.num_blocks);
   };
 
-  // Two LDS stages: while tile i is computed from one stage, tile i+1 is
-  // written into the other and tile i+2 streams into registers; one barrier
-  // per tile.
-  int ids_a[4], ids_b[4];
+  int nid = -1;  // block id of this wave's page of the next step to load
   if (kb0 < kb1) {
-    tile_ids(kb0, ids_a);
-    issue_tile(kb0, ids_a);
-    tile_ids(kb0 + BN, ids_b);
-    store_tile(smem);
-    issue_tile(kb0 + BN, ids_b);
-    tile_ids(kb0 + 2 * BN, ids_a);  // ids are read one tile ahead of their loads
+    issue_step(kb0, page_id(kb0), smem);
+    nid = page_id(kb0 + BN);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
   for (int k0 = kb0, i = 0; k0 < kb1; k0 += BN, ++i) {
     const unsigned char* Ks = smem + (i & 1) * STAGE;
-    const unsigned char* Vt = Ks + BN * KROW;
-    if (wave_active && k0 <= H0 + wrow0 + 31) {  // else the tile is invisible to this wave
+    const unsigned char* Vs = Ks + POOL;
+    if (k0 + BN < kb1) {  // the next step streams into the other stage
+      issue_step(k0 + BN, nid, smem + ((i + 1) & 1) * STAGE);
+      nid = page_id(k0 + 2 * BN);
+    }
+    if (wave_active && k0 <= H0 + wrow0 + 31) {  // else the step is invisible to this wave
       const bool need_mask = (k0 + BN - 1) > (H0 + wrow0);
-      // S^T = K Q^T, two 32-key blocks
-      // the two 32-key blocks accumulate independently: interleave their MFMAs so
-      // the matrix pipe never waits on the previous accumulator of one chain
+      // S^T = K Q^T, two 32-key blocks interleaved so the matrix pipe never
+      // waits on the previous accumulator of one chain
       f32x16_t sacc[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16_t{};
@@ -718,15 +700,17 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, int
       for (int s = 0; s < KS; s += 2) {
         u32x4_t kf[NKB][2];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int r = kb * 32 + pi;
 #pragma unroll
-          for (int t = 0; t < 2; ++t) kf[kb][t] = ld16(Ks + (kb * 32 + pi) * KROW + g * 16 + (s + t) * 32);
+          for (int t = 0; t < 2; ++t) kf[kb][t] = ld16(Ks + r * ROW + (((s + t) * 2 + g) ^ kswz<D>(r)) * 16);
+        }
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) sacc[kb] = mfma_bf16(kf[kb][t], qf[s + t], sacc[kb]);
       }
-      // causal mask on diagonal tiles, running max of the raw scores (the
+      // causal mask on diagonal steps, running max of the raw scores (the
       // positive scale preserves order), weights exp2(scale * (s - max))
       float tmax = -INFINITY;
 #pragma unroll
@@ -769,8 +753,13 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, int
 #pragma unroll
         for (int m = 0; m < NM; ++m) acc[m] *= alpha;
       }
-      // O^T += V^T P^T: for each 16-key slice, the NM channel blocks are
-      // independent accumulators, issued back to back
+      // O^T += V^T P^T for each 16-key slice: lane l of the A operand holds
+      // channel 32 m + l % 32 for keys 8 (l / 32) .. + 7 of the slice, gathered
+      // by two transposing reads (4 keys each): in the 16-lane group q = l / 16,
+      // lane 4 x + y reads the 4 channels 32 m + 16 (q % 2) + 4 y .. + 3 of key
+      // 8 (q / 2) + 4 r + x, and the read hands lane 4 a + b channel
+      // 32 m + 16 (q % 2) + 4 a + b of those 4 keys.
+      const int tq = lane >> 4, tc = lane & 15, tx = tc >> 2, ty = tc & 3;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -778,19 +767,25 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, int
           u32x4_t vf[NM];
 #pragma unroll
           for (int m = 0; m < NM; ++m) {
-            const int d = m * 32 + qc;
-            vf[m] = ld16(Vt + d * VROW + ((kb * 4 + u * 2 + g) ^ vt_swz(d)) * 16);
+            const int d0 = 32 * m + 16 * (tq & 1) + 4 * ty;  // first channel this lane reads
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+              const int row = kb * 32 + 16 * u + 8 * (tq >> 1) + 4 * r + tx;
+              const unsigned char* src =
+                  Vs + row * ROW + (((d0 >> 3) ^ vswz<D>(row)) << 4) + ((d0 & 7) << 1);
+              const u32x2_t t2 = lds_read_tr16(src);
+              vf[m][2 * r] = t2[0];
+              vf[m][2 * r + 1] = t2[1];
+            }
           }
 #pragma unroll
           for (int m = 0; m < NM; ++m) acc[m] = mfma_bf16(vf[m], pk[kb][u], acc[m]);
         }
       }
     }
-    if (k0 + BN < kb1) {
-      store_tile(smem + ((i + 1) & 1) * STAGE);  // tile i+1, loaded during tile i
-      issue_tile(k0 + 2 * BN, ids_a);           // tile i+2 streams in
-      tile_ids(k0 + 3 * BN, ids_a);
-    }
+    // this wave's loads of the next step have landed; after the barrier every
+    // wave's have, and the stage just read is free for the step after
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
 

@@ -96,6 +96,34 @@ __device__ __forceinline__ void st16(void* p, u32x4_t v) { *reinterpret_cast<u32
 __device__ __forceinline__ u32x2_t ld8(const void* p) { return *reinterpret_cast<const u32x2_t*>(p); }
 __device__ __forceinline__ void st8(void* p, u32x2_t v) { *reinterpret_cast<u32x2_t*>(p) = v; }
 
+// ---- gfx950 LDS instructions ----------------------------------------------------------
+// (The host compilation pass does not know these builtins; it sees the bodies
+// only on the device pass.)
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+// Transposing 8-byte LDS read (ds_read_b64_tr_b16): within each group of 16
+// lanes, lane 4x + y names 8 bytes (4 bf16 values); the read hands lane 4a + b
+// value b of the 8-byte pieces named by lanes a, a + 4, a + 8, a + 12, in that
+// order.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const unsigned char* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p));
+#else
+  (void)p;
+  return u32x2_t{0, 0};
+#endif
+}
+// Pool-to-LDS 16-byte load (buffer_load_dwordx4 ... lds): lane i writes LDS
+// bytes dst + 16 i .. + 15 (dst uniform across the wave) with the 16 bytes at
+// buffer offset off of rsrc; an offset past the descriptor's range writes zeros.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, unsigned char* dst, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+#else
+  (void)rsrc; (void)dst; (void)off;
+#endif
+}
+
 // Index of this wave in its workgroup, as a scalar (uniform) value.
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
