@@ -504,14 +504,17 @@ constexpr uint32_t kBf16PairOne = 0x3f803f80u;  // (1.0, 1.0) as a bf16 pair
 
 template <typename T> struct ChunkCfg;
 // bf16: a stage holds a 64-key step of K and of V, both key-major (rows of 2D
-// bytes, no padding); two stages.
+// bytes, no padding).  Two stages, each a __shared__ array of its own (the
+// kernel's `smem` is the first): as distinct objects the compiler can tell
+// that reads of one stage do not alias the loads streaming into the other, and
+// puts no wait for those loads in front of them.
 template <> struct ChunkCfg<bf16_t> {
   template <int D> struct Sizes {
     static constexpr int BN = 64;
     static constexpr int ROW = D * 2;                    // bytes per key row
     static constexpr int POOL = BN * ROW;                // one pool's step
     static constexpr int STAGE = 2 * POOL;               // K, then V
-    static constexpr int BYTES = 2 * STAGE;              // two stages
+    static constexpr int BYTES = STAGE;                  // the first stage
   };
 };
 template <> struct ChunkCfg<float> {
@@ -599,17 +602,19 @@ template <int D> __device__ __forceinline__ int vswz(int r) {
 // transposing LDS reads per MFMA.
 template <int D, bool kSplit, bool kContig, bool kQWait>
 __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, int split, int nsplit,
-                                unsigned char* smem) {
+                                unsigned char* stage_a, unsigned char* stage_b) {
   if constexpr (!kSplit) {
     split = 0;
     nsplit = 1;
   }
   using Cfg = ChunkCfg<bf16_t>::Sizes<D>;
   constexpr int BN = Cfg::BN, NKB = BN / 32, KS = D / 16, NM = D / 32;
-  constexpr int ROW = Cfg::ROW, POOL = Cfg::POOL, STAGE = Cfg::STAGE;
+  constexpr int ROW = Cfg::ROW, POOL = Cfg::POOL;
   constexpr int CPR = D / 8;          // 16-byte chunks per key row
   constexpr int RPI = kWave / CPR;    // rows per wave load instruction (1 KB)
-  constexpr int IPW = kPage / RPI;    // load instructions per wave, per pool and step
+  constexpr int KPW = BN / 4;         // keys of a step each wave loads (one page)
+  constexpr int IPW = KPW / RPI;      // load instructions per wave, per pool and step
+  static_assert(KPW == kPage && KPW % RPI == 0, "each wave loads one page per step");
 
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int qc = lane & 31, g = lane >> 5;
@@ -649,10 +654,25 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, int
   const uint32_t page_bytes = slot_bytes * kPage;
   const uint32_t head_off = static_cast<uint32_t>(kvh) * D * 2;
   const int krow0 = segment_row0<kContig>(a, seg);  // first key row (contiguous K/V)
+  // A wave's page of the step at key k0: page index and the raw block-table
+  // entry (scalar load).  The entry is checked only where it is used, a step
+  // later, so the load's latency is not waited out right after issuing it.
+  struct PageRef { int idx, raw; };
+  auto page_ref = [&](int k0) -> PageRef {
+    const int idx = (k0 >> 4) + w;
+    if constexpr (kContig) return {idx, krow0 + idx * kPage};
+    else return {idx, btrow[min(idx, last_page)]};  // always inside the row
+  };
+  auto page_id = [&](PageRef r) {  // -1 past the range or outside the pool
+    if constexpr (kContig) return r.idx <= last_page ? r.raw : -1;
+    else return (r.idx <= last_page && static_cast<unsigned>(r.raw) < static_cast<unsigned>(a.num_blocks)) ? r.raw : -1;
+  };
   // this lane's part of every load: row (within its wave's page) and chunk
   const int lrow = lane / CPR, lpos = lane % CPR;
-  // loads of the step at key k0 into stage st; id: the block id of this wave's page
-  auto issue_step = [&](int k0, int id, unsigned char* st) {
+  // loads of the step at key k0 into stage st (past the range the descriptor
+  // is empty and the loads write zeros)
+  auto issue_step = [&](int k0, PageRef pr, unsigned char* st) {
+    const int id = page_id(pr);
     const int range = id >= 0 ? static_cast<int>(page_bytes) : 0;
     const auto rk = __builtin_amdgcn_make_buffer_rsrc(page_base<kContig>(a.kc, id, slot_bytes, page_bytes), 0,
                                                       range, kRawBufferWord3);
@@ -660,38 +680,33 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, int
                                                       range, kRawBufferWord3);
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
-      const int r = RPI * j + lrow;  // key within the page (= row within the wave's 16)
-      const int row = 16 * w + r;    // row within the step
+      const int r = RPI * j + lrow;  // key within the page
+      const int row = KPW * w + r;   // row within the step
       const bool in = k0 + row < kb1;
       const uint32_t base = static_cast<uint32_t>(r) * slot_bytes + head_off;
       const uint32_t ok_ = in ? base + static_cast<uint32_t>(lpos ^ kswz<D>(row)) * 16 : kOffsetOutOfRange;
       const uint32_t ov_ = in ? base + static_cast<uint32_t>(lpos ^ vswz<D>(row)) * 16 : kOffsetOutOfRange;
-      unsigned char* dk = st + (16 * w + RPI * j) * ROW;
+      unsigned char* dk = st + (KPW * w + RPI * j) * ROW;
       load_lds16(rk, dk, ok_);
       load_lds16(rv, dk + POOL, ov_);
     }
   };
-  auto page_id = [&](int k0) {  // scalar load; -1 past the range or outside the pool
-    return segment_page<kContig>(btrow, krow0, (k0 >> 4) + w, last_page, a.num_blocks);
-  };
-
-  int nid = -1;  // block id of this wave's page of the next step to load
+  PageRef nref{0, -1};  // this wave's page of the next step to load
   if (kb0 < kb1) {
-    issue_step(kb0, page_id(kb0), smem);
-    nid = page_id(kb0 + BN);
+    issue_step(kb0, page_ref(kb0), stage_a);
+    nref = page_ref(kb0 + BN);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
-  for (int k0 = kb0, i = 0; k0 < kb1; k0 += BN, ++i) {
-    const unsigned char* Ks = smem + (i & 1) * STAGE;
-    const unsigned char* Vs = Ks + POOL;
-    if (k0 + BN < kb1) {  // the next step streams into the other stage
-      issue_step(k0 + BN, nid, smem + ((i + 1) & 1) * STAGE);
-      nid = page_id(k0 + 2 * BN);
-    }
+  // One step: the next step streams into the other stage while this one is
+  // computed from `cur`.
+  auto step = [&](int k0, const unsigned char* cur, unsigned char* nxt) {
+    const unsigned char* Ks = cur;
+    const unsigned char* Vs = cur + POOL;
+    issue_step(k0 + BN, nref, nxt);
     if (wave_active && k0 <= H0 + wrow0 + 31) {  // else the step is invisible to this wave
       const bool need_mask = (k0 + BN - 1) > (H0 + wrow0);
-      // S^T = K Q^T, two 32-key blocks interleaved so the matrix pipe never
+      // S^T = K Q^T, the 32-key blocks interleaved so the matrix pipe never
       // waits on the previous accumulator of one chain
       f32x16_t sacc[NKB];
 #pragma unroll
@@ -783,10 +798,20 @@ __device__ void chunk_tile_bf16(const MainArgs& a, int seg, int h, int tile, int
         }
       }
     }
+    // the block-table entry of the step after next, loaded only now: scalar
+    // loads share the LDS wait counter and complete out of order, so any LDS
+    // wait of this step's compute would have waited for it as well
+    __builtin_amdgcn_sched_barrier(0);
+    nref = page_ref(k0 + 2 * BN);
     // this wave's loads of the next step have landed; after the barrier every
     // wave's have, and the stage just read is free for the step after
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
+  };
+  // two steps per trip, so that each step's stages are fixed objects
+  for (int k0 = kb0; k0 < kb1; k0 += 2 * BN) {
+    step(k0, stage_a, stage_b);
+    if (k0 + BN < kb1) step(k0 + BN, stage_b, stage_a);
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);  // lanes l and l^32 share a row
@@ -1489,6 +1514,9 @@ template <typename T, int D, bool kSplit, bool kContig, bool kDefer>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
   constexpr int kSmem = ChunkCfg<T>::template Sizes<D>::BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kSmem];
+  // the bf16 chunk role's second stage (an object of its own)
+  constexpr bool kBf16 = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) unsigned char smem_b[kBf16 ? ChunkCfg<bf16_t>::Sizes<D>::STAGE : 16];
   __shared__ int s_prefix[2][kLdsSegments + 1];
   __shared__ int s_work[5];
   // scheduler state, touched by thread 0 only; kept in LDS so no register holds
@@ -1684,10 +1712,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
     if (threadIdx.x == 0) s_next = (kDefer && kind == 1) ? kPending : claim();
     if (kind == 1) {
       if (csplit == 1) {
-        if constexpr (sizeof(T) == 2) chunk_tile_bf16<D, false, kContig, kDefer>(a, seg, p1, p2, 0, 1, smem);
+        if constexpr (sizeof(T) == 2) chunk_tile_bf16<D, false, kContig, kDefer>(a, seg, p1, p2, 0, 1, smem, smem_b);
         else chunk_tile_f32<D, false, kContig>(a, seg, p1, p2, 0, 1, smem);
       } else if constexpr (kSplit) {
-        if constexpr (sizeof(T) == 2) chunk_tile_bf16<D, true, kContig, kDefer>(a, seg, p1, p2, p3, csplit, smem);
+        if constexpr (sizeof(T) == 2) chunk_tile_bf16<D, true, kContig, kDefer>(a, seg, p1, p2, p3, csplit, smem, smem_b);
         else chunk_tile_f32<D, true, kContig>(a, seg, p1, p2, p3, csplit, smem);
       }
     } else {
