@@ -238,16 +238,35 @@ __device__ __forceinline__ void append_chunk(const AppendRows& a, long long idx)
   a.k_cache[dst] = kv;
   a.v_cache[dst] = vv;
 }
+// Each thread loads up to kAppendBatch chunks of K and of V before it stores
+// any: the pools may alias the new rows as far as the compiler knows, so
+// loads are never moved above earlier stores by themselves.
+constexpr int kAppendBatch = 4;
 __device__ __forceinline__ void append_row(const AppendRows& a, int t) {
   const int slot = __builtin_amdgcn_readfirstlane(a.slot_mapping[t]);
   if (slot < 0 || slot >= a.pool_slots) return;
   const size_t src = static_cast<size_t>(t) * a.chunks_per_row;
   const size_t dst = static_cast<size_t>(slot) * a.chunks_per_row;
-  for (int c = threadIdx.x; c < a.chunks_per_row; c += kThreads) {
-    const uint4 kv = a.key[src + c];
-    const uint4 vv = a.value[src + c];
-    a.k_cache[dst + c] = kv;
-    a.v_cache[dst + c] = vv;
+  const u32x4_t* key = reinterpret_cast<const u32x4_t*>(a.key);
+  const u32x4_t* value = reinterpret_cast<const u32x4_t*>(a.value);
+  u32x4_t* kc = reinterpret_cast<u32x4_t*>(a.k_cache);
+  u32x4_t* vc = reinterpret_cast<u32x4_t*>(a.v_cache);
+  for (int c0 = 0; c0 < a.chunks_per_row; c0 += kAppendBatch * kThreads) {
+    u32x4_t kv[kAppendBatch], vv[kAppendBatch];
+#pragma unroll
+    for (int u = 0; u < kAppendBatch; ++u) {  // past the row end: a chunk of the row, not stored
+      const int c = min(c0 + u * kThreads + static_cast<int>(threadIdx.x), a.chunks_per_row - 1);
+      kv[u] = key[src + c];
+      vv[u] = value[src + c];
+    }
+#pragma unroll
+    for (int u = 0; u < kAppendBatch; ++u) {
+      const int c = c0 + u * kThreads + static_cast<int>(threadIdx.x);
+      if (c < a.chunks_per_row) {
+        kc[dst + c] = kv[u];
+        vc[dst + c] = vv[u];
+      }
+    }
   }
 }
 

@@ -96,6 +96,8 @@ SPLIT_CASES = [
     ([(300, 6000), (1, 50), (1, 2)], 1, 1, 64, W.F32, 27),
     # fp32, three heads: two sub-groups per head, two of the eight queues empty
     ([(600, 4000), (1, 77), (129, 129)], 3, 3, 64, W.F32, 28),
+    # fp32 at D = 128 with GQA: the split instance at the larger head size
+    ([(1, 500), (260, 3000), (1, 40)], 4, 2, 128, W.F32, 29),
 ]
 
 
