@@ -63,6 +63,7 @@ struct PlanArgs {
   int32_t* tile_prefix;
   int32_t* dec_prefix;
   int32_t* part_prefix;
+  int32_t* tail_prefix;
   int chunk_gsub;  // queue groups per head (chunk_group_items)
   // decode-first workgroups left without a decode item take their first chunk
   // item statically as well (fused fp32 launches, see attn_kernel)
@@ -117,13 +118,16 @@ __device__ int chunk_split_count(const PlanArgs& a, long long csteps, long long 
 // kernel hands out the first item of every workgroup statically (chunk-first
 // workgroup b takes item b / 8 of chunk group b % 8, decode-first workgroup b
 // takes decode item b - chunk_first_wgs); the counters start past those items.
-__device__ void write_plan_header(const PlanArgs& a, int chunk_pairs, int dec_items, int parts,
-                                  int split, int csplit, int bad) {
+__device__ void write_plan_header(const PlanArgs& a, int chunk_pairs, int dec_full, int parts,
+                                  int dec_tail, int split, int csplit, int bad) {
+  const int dec_items = dec_full + dec_tail;
   a.tile_prefix[a.num_seqs] = chunk_pairs;
-  a.dec_prefix[a.num_seqs] = dec_items;
+  a.dec_prefix[a.num_seqs] = dec_full;
   a.part_prefix[a.num_seqs] = parts;
+  a.tail_prefix[a.num_seqs] = dec_tail;
   a.hdr->n_chunk_tiles = chunk_pairs;
   a.hdr->n_dec_items = dec_items;
+  a.hdr->n_dec_full = dec_full;
   a.hdr->n_parts = parts;
   a.hdr->split = split;
   a.hdr->chunk_split = csplit;
@@ -159,8 +163,9 @@ __device__ __forceinline__ void plan_small(const PlanArgs& a) {  // the 64 lanes
   int pick = kSplitCandidates - 1;
   for (int k = 0; k < kSplitCandidates; ++k) {
     const int sh = kSplitMinLog2 + k;
-    const long long n = lq == 1 ? (static_cast<long long>(lk) + (1LL << sh) - 1) >> sh : 0;
-    long long items = n, parts = n > 1 ? n : 0;
+    long long full = 0, tail = 0;
+    if (lq == 1) decode_pieces(lk, sh, full, tail);
+    long long items = full + tail, parts = items > 1 ? items : 0;
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) {
       items += __shfl_xor(items, m);
@@ -218,23 +223,26 @@ __device__ __forceinline__ void plan_small(const PlanArgs& a) {  // the 64 lanes
   }
   const int split_log = kSplitMinLog2 + pick;
   const int split = 1 << split_log;
-  // exclusive prefix sums over the lanes
-  int v[3] = {0, 0, 0};
+  // exclusive prefix sums over the lanes: chunk (tile, range) pairs, decode
+  // full-split items, partial slots, decode tail-piece items
+  int v[4] = {0, 0, 0, 0};
   if (b < a.num_seqs) {
     if (a.sk_out) a.sk_out[b] = lq < 0 ? 0 : lk;
     if (lq >= 2) {
       v[0] = (lq + kChunkRows - 1) / kChunkRows * csplit;
     } else if (lq == 1) {
-      const int n = static_cast<int>((static_cast<unsigned>(lk) + split - 1u) >> split_log);
-      v[1] = n * a.head_groups;
-      v[2] = n > 1 ? n : 0;
+      long long full, tail;
+      decode_pieces(lk, split_log, full, tail);
+      v[1] = static_cast<int>(full) * a.head_groups;
+      v[2] = full + tail > 1 ? static_cast<int>(full + tail) : 0;
+      v[3] = static_cast<int>(tail) * a.head_groups;
     }
   }
-  int incl[3] = {v[0], v[1], v[2]};
+  int incl[4] = {v[0], v[1], v[2], v[3]};
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
 #pragma unroll
-    for (int c = 0; c < 3; ++c) {
+    for (int c = 0; c < 4; ++c) {
       const int o = __shfl_up(incl[c], off);
       if (b >= off) incl[c] += o;
     }
@@ -243,11 +251,12 @@ __device__ __forceinline__ void plan_small(const PlanArgs& a) {  // the 64 lanes
     a.tile_prefix[b] = incl[0] - v[0];
     a.dec_prefix[b] = incl[1] - v[1];
     a.part_prefix[b] = incl[2] - v[2];
+    a.tail_prefix[b] = incl[3] - v[3];
   }
   const int tot0 = __shfl(incl[0], kWave - 1), tot1 = __shfl(incl[1], kWave - 1);
-  const int tot2 = __shfl(incl[2], kWave - 1);
+  const int tot2 = __shfl(incl[2], kWave - 1), tot3 = __shfl(incl[3], kWave - 1);
   const int nbad = __popcll(__ballot(bad));
-  if (b == 0) write_plan_header(a, tot0, tot1, tot2, split, csplit, nbad);
+  if (b == 0) write_plan_header(a, tot0, tot1, tot2, tot3, split, csplit, nbad);
 }
 
 __global__ __launch_bounds__(kWave) void plan_kernel_small(PlanArgs a) { plan_small(a); }
@@ -276,9 +285,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ long long s_parts[32][32];
   __shared__ long long s_cstat[32][4];  // per group: chunk steps, decode keys, chunk tiles, max steps
   __shared__ int s_split_log, s_csplit;
-  __shared__ int s_wave_tot[kPlanThreads / kWave][3];
-  __shared__ int s_carry[3];
-  __shared__ int s_pass_tot[3];
+  __shared__ int s_wave_tot[kPlanThreads / kWave][4];
+  __shared__ int s_carry[4];
+  __shared__ int s_pass_tot[4];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
   const bool cached = a.num_seqs <= kPlanThreads;
@@ -316,9 +325,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
           lq = -1;
         }
         if (lq == 1) {
-          const long long n = (static_cast<long long>(lk) + (1LL << sh) - 1) >> sh;
-          items += n;
-          parts += n > 1 ? n : 0;
+          long long full, tail;
+          decode_pieces(lk, sh, full, tail);
+          items += full + tail;
+          parts += full + tail > 1 ? full + tail : 0;
           dkeys += lk;
         } else if (lq >= 2) {
           const long long nt = (lq + kChunkRows - 1) / kChunkRows;
@@ -362,7 +372,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     const long long n_ct = __shfl(stat, 34), steps_max = __shfl(stat, 35);
     if (tid == 0) {
       s_split_log = fit_mask ? __ffsll(static_cast<long long>(fit_mask)) - 1 : kSplitCandidates - 1;
-      for (int c = 0; c < 3; ++c) s_carry[c] = 0;
+      for (int c = 0; c < 4; ++c) s_carry[c] = 0;
       s_csplit = chunk_split_count(a, csteps, dkeys, n_ct, steps_max);
     }
   }
@@ -371,11 +381,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   const int split = 1 << split_log;
   const int csplit = s_csplit;
 
-  // 2. exclusive prefix sums of chunk tiles, decode items and partial slots.
+  // 2. exclusive prefix sums of chunk tiles, decode full-split items, partial
+  // slots and decode tail-piece items.
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   for (int base = 0; base < a.num_seqs; base += kPlanThreads) {
     const int b = base + tid;
-    int v[3] = {0, 0, 0};
+    int v[4] = {0, 0, 0, 0};
     if (b < a.num_seqs) {
       int lq = my_lq, lk = my_lk;
       if (base > 0 && !plan_segment(a, b, lq, lk)) lq = -1;
@@ -385,24 +396,26 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       } else if (lq >= 2) {
         v[0] = (lq + kChunkRows - 1) / kChunkRows * csplit;  // (query tile, split) pairs per head
       } else if (lq == 1) {
-        const int n = static_cast<int>((static_cast<unsigned>(lk) + split - 1u) >> split_log);
-        v[1] = n * a.head_groups;
-        v[2] = n > 1 ? n : 0;
+        long long full, tail;
+        decode_pieces(lk, split_log, full, tail);
+        v[1] = static_cast<int>(full) * a.head_groups;
+        v[2] = full + tail > 1 ? static_cast<int>(full + tail) : 0;
+        v[3] = static_cast<int>(tail) * a.head_groups;
       }
     }
-    int incl[3] = {v[0], v[1], v[2]};
+    int incl[4] = {v[0], v[1], v[2], v[3]};
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
 #pragma unroll
-      for (int c = 0; c < 3; ++c) {
+      for (int c = 0; c < 4; ++c) {
         const int o = __shfl_up(incl[c], off);
         if (lane >= off) incl[c] += o;
       }
     }
     if (lane == kWave - 1)
-      for (int c = 0; c < 3; ++c) s_wave_tot[wave][c] = incl[c];
+      for (int c = 0; c < 4; ++c) s_wave_tot[wave][c] = incl[c];
     __syncthreads();
-    if (tid < 3) {
+    if (tid < 4) {
       int run = 0;
       for (int w = 0; w < kPlanThreads / kWave; ++w) {
         const int t = s_wave_tot[w][tid];
@@ -416,12 +429,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       a.tile_prefix[b] = s_carry[0] + s_wave_tot[wave][0] + incl[0] - v[0];
       a.dec_prefix[b] = s_carry[1] + s_wave_tot[wave][1] + incl[1] - v[1];
       a.part_prefix[b] = s_carry[2] + s_wave_tot[wave][2] + incl[2] - v[2];
+      a.tail_prefix[b] = s_carry[3] + s_wave_tot[wave][3] + incl[3] - v[3];
     }
     __syncthreads();
-    if (tid < 3) s_carry[tid] += s_pass_tot[tid];
+    if (tid < 4) s_carry[tid] += s_pass_tot[tid];
     __syncthreads();
   }
-  if (tid == 0) write_plan_header(a, s_carry[0], s_carry[1], s_carry[2], split, csplit, s_bad);
+  if (tid == 0)
+    write_plan_header(a, s_carry[0], s_carry[1], s_carry[2], s_carry[3], split, csplit, s_bad);
 }
 
 // ==================================================================== attention
@@ -439,6 +454,7 @@ struct MainArgs {
   const int32_t* tile_prefix;
   const int32_t* dec_prefix;
   const int32_t* part_prefix;
+  const int32_t* tail_prefix;
   float* partials;
   float* chunk_partials;  // [slot][head][128 rows][part_stride] of split chunk tiles
   const int32_t* cu_k;  // contiguous K/V: first row of each segment's keys (else null)
@@ -1110,19 +1126,19 @@ __device__ __forceinline__ void store_row(T* p, const float* v) {
   }
 }
 
+// An item covers keys [kbeg, min(Lk, kbeg + klen)) of 4 query heads of a decode
+// segment; slot < 0: the segment's only item, which writes the output row;
+// else its partial result goes to partial slot part_prefix[seg] + slot.
 template <typename T, int D, bool kContig>
-__device__ void decode_item(const MainArgs& a, int seg, int j, int split_keys) {
+__device__ void decode_item(const MainArgs& a, int seg, int hg, int kbeg, int klen, int slot) {
   constexpr int EPL = D / 16;  // channels per lane
   using Frag = RowFrag<T, EPL>;
   constexpr bool kLateV = Frag::kWords > 4;  // fp32 D=128: load V after the scores
   const int lane = threadIdx.x & 63, w = wave_id();
-  const int head_groups = (a.num_heads + kHeadsPerDecodeItem - 1) / kHeadsPerDecodeItem;
-  const int split = j / head_groups, hg = j - split * head_groups;
   const int h = hg * kHeadsPerDecodeItem + w;
   if (h >= a.num_heads) return;
   const int row = a.cu[seg], Lk = a.sk[seg];
-  const int nsplit = (Lk + split_keys - 1) / split_keys;
-  const int kbeg = split * split_keys, kfin = min(Lk, kbeg + split_keys);
+  const int kfin = min(Lk, kbeg + klen);
   const int r = lane >> 4, c = lane & 15;
   const int kvh = h / a.group;
   const int32_t* btrow = a.bt + static_cast<size_t>(seg) * a.max_blocks;
@@ -1214,7 +1230,7 @@ __device__ void decode_item(const MainArgs& a, int seg, int j, int split_keys) {
     acc[e] += __shfl_xor(acc[e], 16);
     acc[e] += __shfl_xor(acc[e], 32);
   }
-  if (nsplit == 1) {
+  if (slot < 0) {
     if (r == 0) {
       const float inv = 1.f / l_tot;
       float o[EPL];
@@ -1224,7 +1240,7 @@ __device__ void decode_item(const MainArgs& a, int seg, int j, int split_keys) {
     }
   } else {
     float* pp = a.partials +
-                (static_cast<size_t>(a.part_prefix[seg] + split) * a.num_heads + h) * a.part_stride;
+                (static_cast<size_t>(a.part_prefix[seg] + slot) * a.num_heads + h) * a.part_stride;
     if (r == 0) store_row<float, EPL>(pp + 4 + c * EPL, acc);
     if (lane == 0) {
       pp[0] = m_run;
@@ -1315,20 +1331,18 @@ __device__ __forceinline__ void load_step16(KvStep<WPL>& dst, const void* pool, 
 }
 
 template <int D, bool kContig>
-__device__ void decode_item_bf16(const MainArgs& a, int seg, int j, int split_keys, unsigned char* smem) {
+__device__ void decode_item_bf16(const MainArgs& a, int seg, int hg, int kbeg, int klen, int slot,
+                                 unsigned char* smem) {
   constexpr int WPL = D / 32;  // bf16 pairs per lane per key row (8 or 4 channels)
   constexpr int EPL = 2 * WPL;
   const int lane = threadIdx.x & 63, w = wave_id();
-  const int head_groups = (a.num_heads + kHeadsPerDecodeItem - 1) / kHeadsPerDecodeItem;
-  const int split = j / head_groups, hg = j - split * head_groups;
   const int r = lane >> 4, c = lane & 15;
   // rows past the last head (num_heads not a multiple of 4) read the group's
   // first head and are dropped at the end
   const int h = hg * kHeadsPerDecodeItem + r;
   const int hq = h < a.num_heads ? h : hg * kHeadsPerDecodeItem;
   const int row = a.cu[seg], Lk = a.sk[seg];
-  const int nsplit = (Lk + split_keys - 1) / split_keys;
-  const int kbeg = split * split_keys, kfin = min(Lk, kbeg + split_keys);
+  const int kfin = min(Lk, kbeg + klen);
   const int kvh = hq / a.group;
   const_i32_t* btrow = (const_i32_t*)(a.bt) + static_cast<size_t>(seg) * a.max_blocks;
   const uint32_t slot_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 2;
@@ -1472,7 +1486,7 @@ __device__ void decode_item_bf16(const MainArgs& a, int seg, int j, int split_ke
 #pragma unroll
       for (int e = 0; e < CPL; ++e) o[e] = fmaf(src[e], f, o[e]);
     }
-    if (nsplit == 1) {
+    if (slot < 0) {
       const float inv = 1.f / l_tot;
       bf16_t* op = static_cast<bf16_t*>(a.out) + (static_cast<size_t>(row) * a.num_heads + hm) * D + ch;
       if constexpr (CPL == 2) {
@@ -1482,7 +1496,7 @@ __device__ void decode_item_bf16(const MainArgs& a, int seg, int j, int split_ke
       }
     } else {
       float* pp = a.partials +
-                  (static_cast<size_t>(a.part_prefix[seg] + split) * a.num_heads + hm) * a.part_stride;
+                  (static_cast<size_t>(a.part_prefix[seg] + slot) * a.num_heads + hm) * a.part_stride;
 #pragma unroll
       for (int e = 0; e < CPL; ++e) pp[4 + ch + e] = o[e];
       if (lane == 0) {
@@ -1517,8 +1531,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
   // the bf16 chunk role's second stage (an object of its own)
   constexpr bool kBf16 = sizeof(T) == 2;
   __shared__ __attribute__((aligned(16))) unsigned char smem_b[kBf16 ? ChunkCfg<bf16_t>::Sizes<D>::STAGE : 16];
-  __shared__ int s_prefix[2][kLdsSegments + 1];
-  __shared__ int s_work[5];
+  __shared__ int s_prefix[3][kLdsSegments + 1];  // chunk pairs, decode full splits, decode tail pieces
+  __shared__ int s_work[6];
   // scheduler state, touched by thread 0 only; kept in LDS so no register holds
   // it across work items
   __shared__ int s_next;           // item claimed for the next iteration
@@ -1526,7 +1540,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
   __shared__ int s_dec_open;
   const int n_tiles = a.hdr->n_chunk_tiles;
   const int n_dec = a.hdr->n_dec_items;
+  const int n_dec_full = a.hdr->n_dec_full;
   const int split_keys = a.hdr->split;
+  const int head_groups = (a.num_heads + kHeadsPerDecodeItem - 1) / kHeadsPerDecodeItem;
   const int csplit = kSplit ? a.hdr->chunk_split : 1;
   const int gsub = sizeof(T) == 4 ? a.hdr->chunk_gsub : 1;  // bf16 planners always write 1
   const bool lds_lookup = a.num_seqs <= kLdsSegments;
@@ -1534,6 +1550,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
     for (int i = threadIdx.x; i <= a.num_seqs; i += kThreads) {
       s_prefix[0][i] = a.tile_prefix[i];
       s_prefix[1][i] = a.dec_prefix[i];
+      s_prefix[2][i] = a.tail_prefix[i];
     }
   }
   // Work distribution.  Decode splits come from one queue; chunk tiles from
@@ -1657,12 +1674,35 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
     if (threadIdx.x == 0) {
       if (kDefer && s_next == kPending) s_next = claim();  // claim deferred by a chunk item
       const int cur = s_next;
-      int kind = 0, seg = 0, p1 = 0, p2 = 0, p3 = 0;  // kind: 0 done, 1 chunk, 2 decode
+      int kind = 0, seg = 0, p1 = 0, p2 = 0, p3 = 0, p4 = 0;  // kind: 0 done, 1 chunk, 2 decode
       if (cur != kDone && (cur & kDecodeTag)) {
+        // full splits first (dec_prefix), then the tail pieces (tail_prefix),
+        // both segment by segment with the head groups innermost: item ->
+        // head group p1, keys [p2, p2 + p3), partial slot p4 (-1: the segment's
+        // only item writes the output row)
         const int d = cur & (kDecodeTag - 1);
-        seg = lds_lookup ? find_segment_lds(s_prefix[1], a.num_seqs, d)
-                         : find_segment(a.dec_prefix, a.num_seqs, d);
-        p1 = d - (lds_lookup ? s_prefix[1][seg] : a.dec_prefix[seg]);
+        const bool tail = d >= n_dec_full;
+        const int e = tail ? d - n_dec_full : d;
+        auto resolve = [&](const int* dp, const int* tp) {  // LDS copies or the workspace arrays
+          const int* ep = tail ? tp : dp;
+          int lo = 0, hi = a.num_seqs;  // segment owning item e: ep[lo] <= e < ep[hi]
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (ep[mid] <= e) lo = mid; else hi = mid;
+          }
+          seg = lo;
+          const int local = e - ep[seg];
+          const int piece = local / head_groups;
+          const int nfull = (dp[seg + 1] - dp[seg]) / head_groups;
+          const int ntail = (tp[seg + 1] - tp[seg]) / head_groups;
+          const int tail_keys = split_keys >> kTailLog2;
+          p1 = local - piece * head_groups;
+          p2 = tail ? nfull * split_keys + piece * tail_keys : piece * split_keys;
+          p3 = tail ? tail_keys : split_keys;
+          p4 = nfull + ntail == 1 ? -1 : (tail ? nfull + piece : piece);
+        };
+        if (lds_lookup) resolve(s_prefix[1], s_prefix[2]);
+        else resolve(a.dec_prefix, a.tail_prefix);
         kind = 2;
       } else if (cur != kDone) {
         // group x holds, segment by segment, (head x + 8k, tile, split) for its
@@ -1694,6 +1734,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
       s_work[2] = p1;
       s_work[3] = p2;
       s_work[4] = p3;
+      s_work[5] = p4;
     }
     __syncthreads();
     // the work item is uniform across the workgroup: keep it in scalar registers so
@@ -1703,6 +1744,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
     const int p1 = __builtin_amdgcn_readfirstlane(s_work[2]);
     const int p2 = __builtin_amdgcn_readfirstlane(s_work[3]);
     const int p3 = __builtin_amdgcn_readfirstlane(s_work[4]);
+    const int p4 = __builtin_amdgcn_readfirstlane(s_work[5]);
     __syncthreads();
     if (kind == 0) break;
     // the next item, claimed while this one runs (hides the atomic's latency),
@@ -1719,8 +1761,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
         else chunk_tile_f32<D, true, kContig>(a, seg, p1, p2, p3, csplit, smem);
       }
     } else {
-      if constexpr (sizeof(T) == 2) decode_item_bf16<D, kContig>(a, seg, p1, split_keys, smem);
-      else decode_item<T, D, kContig>(a, seg, p1, split_keys);
+      if constexpr (sizeof(T) == 2) decode_item_bf16<D, kContig>(a, seg, p1, p2, p3, p4, smem);
+      else decode_item<T, D, kContig>(a, seg, p1, p2, p3, p4);
     }
   }
 }
@@ -1967,6 +2009,7 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
   int32_t* tile_prefix = reinterpret_cast<int32_t*>(ws + L.ws.tile_prefix);
   int32_t* dec_prefix = reinterpret_cast<int32_t*>(ws + L.ws.dec_prefix);
   int32_t* part_prefix = reinterpret_cast<int32_t*>(ws + L.ws.part_prefix);
+  int32_t* tail_prefix = reinterpret_cast<int32_t*>(ws + L.ws.tail_prefix);
   int32_t* seqlens = reinterpret_cast<int32_t*>(ws + L.ws.seqlens);
   const int head_groups = (L.num_heads + kHeadsPerDecodeItem - 1) / kHeadsPerDecodeItem;
 
@@ -1979,7 +2022,7 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
               grid, L.ws.tiles_cap, split_ok ? L.ws.chunk_slots_cap : 0, chunk_first_wgs,
               dec_first_wgs, split_items, chunk_step_cost, kContig ? L.cu_seqlens_k : nullptr,
               L.total_k, kContig ? seqlens : nullptr, hdr, tile_prefix, dec_prefix, part_prefix,
-              chunk_group_sub(sizeof(T) == 4, L.num_heads),
+              tail_prefix, chunk_group_sub(sizeof(T) == 4, L.num_heads),
               sizeof(T) == 4 && L.launch_mode == kLaunchFused ? 1 : 0};
   // hybrid_step_fwd: the append first -- with the small planner in the same
   // launch when the step has few segments, else on its own
@@ -2013,7 +2056,7 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
               kContig ? seqlens : L.seqlens_k, L.block_table,
               L.num_seqs, L.num_heads, L.num_kv_heads, L.num_heads / L.num_kv_heads,
               L.num_blocks, L.max_blocks, L.ws.part_stride, L.sm_scale * kLog2e, hdr,
-              tile_prefix, dec_prefix, part_prefix,
+              tile_prefix, dec_prefix, part_prefix, tail_prefix,
               reinterpret_cast<float*>(ws + L.ws.partials),
               reinterpret_cast<float*>(ws + L.ws.chunk_partials), L.cu_seqlens_k, 3, half};
   // Deferred chunk claims (kDefer): always for fp32; for bf16 when the longest

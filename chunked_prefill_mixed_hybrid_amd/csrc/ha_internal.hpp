@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "ha_common.hpp"
+
 namespace ha {
 
 // ---- tuning constants (gfx950) ---------------------------------------------------
@@ -19,6 +21,24 @@ constexpr int kPartsMax = 16384;    // cap on (segment, split) partial slots
 constexpr int kItemsPerSlot = 16;   // decode work items aimed at per resident workgroup
 constexpr int kHeadsPerDecodeItem = 4;  // bf16: one head per 16-lane row of every wave; fp32: one per wave
 constexpr int kMaxSeqlenK = 1 << 30;
+// Decode tail: when the decode split is at least 2^kTailMinLog2 keys, each
+// segment's last split is cut into pieces of split / 2^kTailLog2 keys that are
+// queued after every full split, so the queue ends with short items instead
+// of full ones (fewer workgroups idle while the last items finish).
+constexpr int kTailMinLog2 = 11;
+constexpr int kTailLog2 = 2;
+// Full splits and tail pieces of a decode segment of lk keys at split 2^sh.
+__host__ __device__ inline void decode_pieces(long long lk, int sh, long long& full, long long& tail) {
+  const long long n = (lk + (1LL << sh) - 1) >> sh;
+  if (sh >= kTailMinLog2 && n >= 1) {
+    full = n - 1;
+    const long long piece = 1LL << (sh - kTailLog2);
+    tail = (lk - (full << sh) + piece - 1) >> (sh - kTailLog2);
+  } else {
+    full = n;
+    tail = 0;
+  }
+}
 // Chunk tiles are split along the keys only when a few long tiles would
 // otherwise outlast the rest of the step: at most this many (tile, head, split)
 // items in all (kChunkSplitItems; the one-wave planner counts only non-empty
@@ -37,6 +57,7 @@ __host__ __device__ inline int chunk_range_keys(int lk, int nsplit) {
 
 // ---- workspace ---------------------------------------------------------------------
 // [header 256 B][tile_prefix (B+1)][dec_prefix (B+1)][part_prefix (B+1)][seqlens (B+1)]
+// [tail_prefix (B+1)]
 // [partials parts_cap x H x (D + 4) fp32]
 // [chunk_partials chunk_slots_cap x H x 128 x (D + 4) fp32]; every array starts
 // on a 256-byte boundary.
@@ -88,20 +109,21 @@ struct PlanHeader {
   uint32_t chunk_counter[kXcdGroups];  // next chunk item of each group (set by the planner)
   uint32_t dec_counter;   // next decode item (set by the planner each call)
   int32_t n_chunk_tiles;  // query tiles (per head) over all chunk segments
-  int32_t n_dec_items;    // decode (segment, split, 4-head group) items
+  int32_t n_dec_items;    // decode (segment, split or tail piece, 4-head group) items
+  int32_t n_dec_full;     // of which full splits (queued first; the tail pieces follow)
   int32_t split;          // decode split size in keys (multiple of 64)
   int32_t n_parts;        // partial slots in use
   int32_t bad_segments;   // segments skipped because they broke a precondition
   int32_t chunk_split;    // KV splits per chunk tile (1: tiles are not split)
   int32_t chunk_gsub;     // queue groups per head (chunk_group_items)
-  int32_t pad[48];
+  int32_t pad[47];
 };
 static_assert(sizeof(PlanHeader) == 256, "header is 256 bytes");
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t tile_prefix, dec_prefix, part_prefix, seqlens, partials, chunk_partials, total;
+  size_t tile_prefix, dec_prefix, part_prefix, seqlens, tail_prefix, partials, chunk_partials, total;
   int parts_cap;
   int part_stride;      // floats per (part, head) or (chunk slot, head, row): m, l, 2 pad, acc[D]
   int tiles_cap;        // bound on query tiles over all chunk segments
@@ -138,6 +160,7 @@ inline WsLayout ws_layout(int num_seqs, int total_q, int max_seqlen_k, int num_h
   l.dec_prefix = off; off += arr;
   l.part_prefix = off; off += arr;
   l.seqlens = off; off += arr;  // Lk per segment, derived by the planner for contiguous K/V
+  l.tail_prefix = off; off += arr;  // decode tail pieces (x head groups) per segment
   l.parts_cap = parts_cap_for(num_seqs, max_seqlen_k);
   l.part_stride = head_dim + 4;
   l.partials = off;

@@ -45,8 +45,8 @@ def gpu_step(ds: W.DeviceStep, workspace=None, append=True):
     return out
 
 
-PLAN_HEADER_FIELDS = ("dec_counter", "n_chunk_tiles", "n_dec_items", "split", "n_parts",
-                      "bad_segments", "chunk_split")
+PLAN_HEADER_FIELDS = ("dec_counter", "n_chunk_tiles", "n_dec_items", "n_dec_full", "split",
+                      "n_parts", "bad_segments", "chunk_split")
 
 
 def plan_header(workspace) -> dict:

@@ -76,6 +76,22 @@ int main() {
         return fail("range length", lk, s, ck);
     }
   }
+  // decode full splits and tail pieces tile a segment exactly: full splits of
+  // 2^sh keys, then pieces of 2^(sh - kTailLog2), the last one non-empty
+  for (long long lk = 1; lk <= 300000; lk += (lk < 5000 ? 1 : 997)) {
+    for (int sh = kSplitMinLog2; sh < kSplitMinLog2 + kSplitCandidates; ++sh) {
+      long long full, tail;
+      decode_pieces(lk, sh, full, tail);
+      const long long n = (lk + (1LL << sh) - 1) >> sh;
+      if (sh < kTailMinLog2) {
+        if (full != n || tail != 0) return fail("no tail below the threshold", lk, sh, tail);
+        continue;
+      }
+      const long long piece = 1LL << (sh - kTailLog2), covered = (full << sh) + tail * piece;
+      if (full != n - 1 || tail < 1 || tail > (1LL << kTailLog2) || covered < lk || covered - piece >= lk)
+        return fail("tail pieces", lk, sh, tail);
+    }
+  }
   // workspace bounds on random steps: query tiles of the chunk segments, decode
   // partial slots at the smallest split, 256-byte aligned arrays in order
   std::mt19937 rng(7);
@@ -99,8 +115,9 @@ int main() {
     if (parts > pc && pc < kPartsMax) return fail("parts_cap_for", b, max_k, parts);
     const int hq = 1 + static_cast<int>(rng() % 64), d = (rng() & 1) ? 64 : 128;
     const WsLayout l = ws_layout(b, static_cast<int>(total_q), max_k, hq, d);
-    const size_t offs[] = {l.tile_prefix, l.dec_prefix, l.part_prefix, l.seqlens, l.partials, l.chunk_partials, l.total};
-    for (int i = 0; i < 7; ++i) {
+    const size_t offs[] = {l.tile_prefix, l.dec_prefix, l.part_prefix, l.seqlens, l.tail_prefix, l.partials,
+                           l.chunk_partials, l.total};
+    for (int i = 0; i < 8; ++i) {
       if (offs[i] % 256 != 0) return fail("workspace array alignment", b, i, static_cast<long long>(offs[i]));
       if (i > 0 && offs[i] < offs[i - 1]) return fail("workspace arrays out of order", b, i, 0);
     }

@@ -333,7 +333,7 @@ def _edge_rows(n, rng, extra=6):
     return sorted(base)
 
 
-def _config_parity(config, extra_chunk_rows, batch_bytes=4 << 30):
+def _config_parity(config, extra_chunk_rows, batch_bytes=4 << 30, require_tail=False):
     """Whole-pool append check plus oracle parity of EVERY decode row (all
     heads) and of the first and last row of every chunk tile (plus random
     rows) of a big workload step.  Pages reach the host a few segments at a
@@ -346,7 +346,13 @@ def _config_parity(config, extra_chunk_rows, batch_bytes=4 << 30):
     hkv, d = spec.num_kv_heads, spec.head_dim
     k_before, v_before = ds.k_cache.clone(), ds.v_cache.clone()
     G.note(f"config{config}: GPU step ({meta.num_seqs} segments, {meta.total_q} rows)")
-    out = G.gpu_step(ds)
+    ws = B.alloc_workspace(meta.num_seqs, meta.total_q, meta.max_seqlen_k, spec.num_heads, d)
+    out = G.gpu_step(ds, workspace=ws)
+    hdr = _check_plan_arrays(ws, meta, spec.num_heads)
+    G.note(f"config{config}: decode split {hdr['split']}, {hdr['n_dec_full']} full-split items, "
+           f"{hdr['n_dec_items'] - hdr['n_dec_full']} tail-piece items")
+    if require_tail:
+        assert hdr["n_dec_items"] > hdr["n_dec_full"], hdr
     sel_rows = np.zeros(meta.total_q, np.uint8)
     for b in range(meta.num_seqs):
         r0, n = int(meta.cu_seqlens_q[b]), int(lq[b])
@@ -404,7 +410,7 @@ def test_config3_decode_heavy():
 
 @pytest.mark.timeout(900)
 def test_config4_long_context():
-    _config_parity(4, 4)
+    _config_parity(4, 4, require_tail=True)  # long decodes: the queue ends with tail pieces
 
 
 @pytest.mark.timeout(900)
@@ -434,26 +440,44 @@ def test_many_segments_budget_step():
     kc, vc = G.host_pools(ds)
     assert kc.tobytes() == kc_ref.tobytes() and vc.tobytes() == vc_ref.tobytes()
     G.compare(G.to_f64(out), ref, W.BF16, "many segments")
-    # planner output: exclusive prefix sums of (tile, split) pairs per head,
-    # decode items and decode partial slots, per segment
+    _check_plan_arrays(ws, meta, hq)
+    del ds
+    _free()
+
+
+def _check_plan_arrays(ws, meta, hq):
+    """The planner's per-segment arrays in the workspace (after the 256-byte
+    header: chunk (tile, range) pairs per head, decode full-split items,
+    partial slots, key lengths, decode tail-piece items) against their
+    definitions: a decode segment of Lk keys at split S has ceil(Lk / S) full
+    splits, or, when S >= 2048, ceil(Lk / S) - 1 full splits and the rest in
+    pieces of S / 4 keys; each split or piece is one item per group of 4
+    heads; partial slots are needed when a segment has more than one."""
     hdr = G.plan_header(ws)
     nseg = meta.num_seqs
     arr = (4 * (nseg + 1) + 255) // 256 * 256
-    raw = ws[256:256 + 3 * arr].cpu().numpy().view(np.int32)
-    tile_p, dec_p, part_p = (raw[k * arr // 4:k * arr // 4 + nseg + 1] for k in range(3))
+    raw = ws[256:256 + 5 * arr].cpu().numpy().view(np.int32)
+    tile_p, dec_p, part_p, _, tail_p = (raw[k * arr // 4:k * arr // 4 + nseg + 1] for k in range(5))
     lqs = np.diff(meta.cu_seqlens_q).astype(np.int64)
     lks = meta.seqlens_k.astype(np.int64)
     split, cs = hdr["split"], hdr["chunk_split"]
     head_groups = (hq + 3) // 4
-    n_dec = np.where(lqs == 1, (lks + split - 1) // split, 0)
-    want = [np.where(lqs >= 2, (lqs + 127) // 128 * cs, 0), n_dec * head_groups,
-            np.where(n_dec > 1, n_dec, 0)]
-    for got_p, w_p, name in zip((tile_p, dec_p, part_p), want, ("tile", "decode", "partial")):
+    n = np.where(lqs == 1, (lks + split - 1) // split, 0)
+    if split >= 2048:
+        full = np.maximum(n - 1, 0)
+        piece = split // 4
+        tail = np.where(lqs == 1, (lks - full * split + piece - 1) // piece, 0)
+    else:
+        full, tail = n, np.zeros_like(n)
+    want = [np.where(lqs >= 2, (lqs + 127) // 128 * cs, 0), full * head_groups,
+            np.where(full + tail > 1, full + tail, 0), tail * head_groups]
+    for got_p, w_p, name in zip((tile_p, dec_p, part_p, tail_p), want,
+                                ("tile", "decode", "partial", "tail")):
         ex = np.concatenate([[0], np.cumsum(w_p)])
-        assert np.array_equal(got_p.astype(np.int64), ex), name
-    assert hdr["n_dec_items"] == int(dec_p[-1]) and hdr["bad_segments"] == 0
-    del ds
-    _free()
+        assert np.array_equal(got_p.astype(np.int64), ex), (name, split)
+    assert hdr["n_dec_full"] == int(dec_p[-1]) and hdr["bad_segments"] == 0
+    assert hdr["n_dec_items"] == int(dec_p[-1]) + int(tail_p[-1])
+    return hdr
 
 
 # ---------------------------------------------------------------- chunk invariance

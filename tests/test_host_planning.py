@@ -15,7 +15,8 @@ pytestmark = pytest.mark.skipif(not os.path.exists(build.hipcc()), reason="hipcc
 def test_host_planning(tmp_path: Path):
     src = Path(__file__).with_name("host_planning_check.cpp")
     exe = tmp_path / "host_planning_check"
-    res = subprocess.run([build.hipcc(), "-std=c++17", "-O2", f"-I{build.CSRC}", f"-I{build.INCLUDE}",
+    res = subprocess.run([build.hipcc(), f"--offload-arch={build.ARCH}", "-std=c++17", "-O2",
+                          f"-I{build.CSRC}", f"-I{build.INCLUDE}",
                           str(src), "-o", str(exe)], capture_output=True, text=True)
     assert res.returncode == 0, res.stdout + res.stderr
     run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
