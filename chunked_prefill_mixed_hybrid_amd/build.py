@@ -27,6 +27,11 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # never emit packed fp32 VALU ops (v_pk_*_f32): plain fp32 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the one-segment prefill kernel rescales its
+    # output accumulators with VALU multiplies, and with AGPR accumulators the
+    # compiler copied all 128 of them out and back on every key block, taken
+    # branch or not (the other kernels compile to the same code either way)
+    "-mllvm", "--amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

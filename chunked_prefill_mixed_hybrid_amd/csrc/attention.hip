@@ -515,6 +515,9 @@ __device__ __forceinline__ int segment_row0(const MainArgs& a, int seg) {
 // s_waitcnt operand (gfx9 encoding) that waits for every outstanding vector
 // memory load and nothing else: vmcnt 0, expcnt 7, lgkmcnt 15.
 constexpr int kWaitVmcnt0 = 0x0F70;
+// ... and the one that waits until at most n vector memory loads are
+// outstanding (vmcnt is split: bits 3:0 and 15:14)
+constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 constexpr uint32_t kBf16PairOne = 0x3f803f80u;  // (1.0, 1.0) as a bf16 pair
 
@@ -1912,6 +1915,382 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(MainArgs a) {
   }
 }
 
+// ==================================================================== one-segment prefill, bf16
+// A step that is a single prefill chunk (one segment) has no decode work to
+// share the CUs with, so it runs a kernel shaped for the matrix cores alone:
+// each wave owns 64 query rows (two 32-row blocks that share every K and V
+// operand read, so a step's LDS reads serve twice the MFMA work of the fused
+// kernel's 32-row waves), a tile is 256 rows x one head, a workgroup holds a
+// whole CU (one wave per SIMD, up to 512 registers: the O accumulators go to
+// AGPRs) and four LDS stages keep K/V loads two steps ahead.  With one wave
+// per SIMD nothing else hides the softmax, so the step is software pipelined:
+// each block's softmax is scheduled among MFMAs of the other phase.  Same data
+// layout, swizzles, masks and online softmax as chunk_tile_bf16.
+constexpr int kPrefillBlocks = 2;                          // 32-row blocks per wave
+constexpr int kPrefillRows = 4 * 32 * kPrefillBlocks;      // query rows per tile
+
+struct PrefillArgs {
+  MainArgs m;
+  int total_q, max_q, max_k, total_k, ntiles;
+};
+
+// Keys [0, Lk) of segment 0 and whether it meets the documented preconditions
+// (the planner's test for every segment); a segment that does not is skipped.
+template <bool kContig>
+__device__ __forceinline__ bool prefill_segment(const PrefillArgs& p, int& q0, int& lq, int& lk) {
+  const MainArgs& a = p.m;
+  const int c0 = a.cu[0], c1 = a.cu[1];
+  q0 = c0;
+  lq = c1 - c0;
+  bool rows_ok = true;
+  if constexpr (kContig) {
+    const int k0 = a.cu_k[0], k1 = a.cu_k[1];
+    lk = k1 - k0;
+    rows_ok = k0 >= 0 && k1 <= p.total_k;
+  } else {
+    lk = a.sk[0];
+  }
+  return rows_ok && c0 >= 0 && c1 >= c0 && c1 <= p.total_q && lq <= lk && lk <= p.max_k && lq <= p.max_q &&
+         ((lk + kPage - 1) / kPage) <= a.max_blocks;
+}
+
+template <int D, bool kContig>
+__device__ void prefill_tile_bf16(const MainArgs& a, int h, int tile, int q0, int Lq, int Lk,
+                                  unsigned char* st0, unsigned char* st1, unsigned char* st2,
+                                  unsigned char* st3) {
+  using Cfg = ChunkCfg<bf16_t>::Sizes<D>;
+  constexpr int BN = Cfg::BN, NKB = BN / 32, KS = D / 16, NM = D / 32, RB = kPrefillBlocks;
+  static_assert(RB == 2, "the pipeline below pairs the two row blocks");
+  constexpr int ROW = Cfg::ROW, POOL = Cfg::POOL;
+  constexpr int CPR = D / 8;          // 16-byte chunks per key row
+  constexpr int RPI = kWave / CPR;    // rows per wave load instruction (1 KB)
+  constexpr int KPW = BN / 4;         // keys of a step each wave loads (one page)
+  constexpr int IPW = KPW / RPI;      // load instructions per wave, per pool and step
+  static_assert(KPW == kPage && KPW % RPI == 0, "each wave loads one page per step");
+  // s_waitcnt operands: all vector loads but the last one / two steps' landed
+  constexpr int kWaitOneStep = wait_vmcnt(2 * IPW);
+  constexpr int kWaitTwoSteps = wait_vmcnt(4 * IPW);
+
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int qc = lane & 31, g = lane >> 5;
+  const int H0 = Lk - Lq;
+  const int kvh = h / a.group;
+  const int row0 = tile * kPrefillRows;
+  const int rows_end = min(row0 + kPrefillRows, Lq);
+  const int kb1 = H0 + rows_end;  // keys [0, kb1) are visible to some row of the tile
+  const int nsteps = (kb1 + BN - 1) / BN;
+  const int wrow0 = row0 + w * 32 * RB;
+  const int pi = key_perm(qc);
+
+  // Q^T operands: for row block r, lane supplies Q[wrow0 + 32 r + qc][s*16 + g*8 .. +8]
+  u32x4_t qf[RB][KS];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const int row = wrow0 + 32 * r + qc;
+    const bool ok = row < Lq;
+    const bf16_t* qp = static_cast<const bf16_t*>(a.q) +
+                       (static_cast<size_t>(q0 + (ok ? row : 0)) * a.num_heads + h) * D + g * 8;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[r][s] = ok ? ld16(qp + s * 16) : u32x4_t{0, 0, 0, 0};
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+  f32x16_t acc[RB][NM];
+  float m_run[RB], l_run[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) acc[r][m] = f32x16_t{};
+    m_run[r] = -INFINITY;
+    l_run[r] = 0.f;
+  }
+
+  const_i32_t* btrow = (const_i32_t*)(a.bt);  // segment 0's row of the block table
+  const int last_page = (max(kb1, 1) - 1) >> 4;
+  const uint32_t slot_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 2;
+  const uint32_t page_bytes = slot_bytes * kPage;
+  const uint32_t head_off = static_cast<uint32_t>(kvh) * D * 2;
+  const int krow0 = kContig ? a.cu_k[0] : 0;
+  struct PageRef { int idx, raw; };
+  auto page_ref = [&](int k0) -> PageRef {
+    const int idx = (k0 >> 4) + w;
+    if constexpr (kContig) return {idx, krow0 + idx * kPage};
+    else return {idx, btrow[min(idx, last_page)]};  // always inside the row
+  };
+  auto page_id = [&](PageRef r) {  // -1 past the range or outside the pool
+    if constexpr (kContig) return r.idx <= last_page ? r.raw : -1;
+    else return (r.idx <= last_page && static_cast<unsigned>(r.raw) < static_cast<unsigned>(a.num_blocks)) ? r.raw : -1;
+  };
+  const int lrow = lane / CPR, lpos = lane % CPR;
+  auto issue_step = [&](int k0, PageRef pr, unsigned char* st) {
+    const int id = page_id(pr);
+    const int range = id >= 0 ? static_cast<int>(page_bytes) : 0;
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(page_base<kContig>(a.kc, id, slot_bytes, page_bytes), 0,
+                                                      range, kRawBufferWord3);
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc(page_base<kContig>(a.vc, id, slot_bytes, page_bytes), 0,
+                                                      range, kRawBufferWord3);
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      const int r = RPI * j + lrow;  // key within the page
+      const int row = KPW * w + r;   // row within the step
+      const bool in = k0 + row < kb1;
+      const uint32_t base = static_cast<uint32_t>(r) * slot_bytes + head_off;
+      const uint32_t ok_ = in ? base + static_cast<uint32_t>(lpos ^ kswz<D>(row)) * 16 : kOffsetOutOfRange;
+      const uint32_t ov_ = in ? base + static_cast<uint32_t>(lpos ^ vswz<D>(row)) * 16 : kOffsetOutOfRange;
+      unsigned char* dk = st + (KPW * w + RPI * j) * ROW;
+      load_lds16(rk, dk, ok_);
+      load_lds16(rv, dk + POOL, ov_);
+    }
+  };
+
+  // ---- the pieces of the pipeline, per half step (32 keys, key block kb)
+  // LDS operand addresses.  K: chunk (2s + g) of step row 32 kb + pi sits at
+  // chunk (2s + g) ^ z, z = kswz(pi), i.e. at byte
+  //   32 kb ROW + (kofs ^ 32 s),  kofs = pi ROW + 16 (g ^ (z & 1)) + 32 (z >> 1)
+  // (32 s and 32 (z >> 1) share bits 5..7, which nothing else uses).  V: the
+  // transposing read of (kb, u, r, m) is at
+  //   (32 kb + 16 u + 4 r) ROW + (vofs ^ 64 m)
+  // with vofs the lane's part (see pv).  Both offsets pass through an empty asm
+  // statement at every use, so the compiler recomputes the few XORs instead of
+  // keeping an address register per (stage, s) or (stage, m).
+  const int kz = kswz<D>(pi);
+  const uint32_t kofs0 = static_cast<uint32_t>(pi * ROW + 16 * (g ^ (kz & 1)) + 32 * (kz >> 1));
+  const int tq = lane >> 4, tc = lane & 15, tx = tc >> 2, ty = tc & 3;
+  const int vz = vswz<D>(8 * (tq >> 1) + tx);
+  const int vx = 2 * (tq & 1) + (ty >> 1);
+  const uint32_t vofs0 = static_cast<uint32_t>((8 * (tq >> 1) + tx) * ROW + 16 * (vx ^ (vz & 3)) +
+                                               8 * (ty & 1) + 64 * (vz >> 2));
+  // the K operands of one key block, into registers
+  auto load_k = [&](const unsigned char* Ks, int kb, u32x4_t (&kf)[KS]) {
+    uint32_t kofs = kofs0;
+    asm volatile("" : "+v"(kofs));
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kf[s] = ld16(Ks + kb * 32 * ROW + (kofs ^ static_cast<uint32_t>(32 * s)));
+  };
+  // S_r = K Q_r^T of one key block for both row blocks, each K operand used
+  // by both
+  auto qk = [&](const u32x4_t (&kf)[KS], f32x16_t& s0, f32x16_t& s1) {
+    s0 = s1 = f32x16_t{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      s0 = mfma_bf16(kf[s], qf[0][s], s0);
+      s1 = mfma_bf16(kf[s], qf[1][s], s1);
+    }
+  };
+  // causal mask of the key block starting at key kbase (value v is key
+  // kbase + 16 (v / 8) + 8 g + v % 8), for blocks past this wave's first
+  // diagonal; it also blanks blocks past the wave's (or the tile's) last row
+  auto mask = [&](int kbase, f32x16_t& sc, int r) {
+    const int lim = H0 + wrow0 + 32 * r + qc - kbase - (g << 3);
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      if (((v >> 3) << 4) + (v & 7) > lim) sc[v] = -INFINITY;
+  };
+  // online softmax of row block r over one key block: weights as bf16 pairs
+  // (P^T operands), the reference max and the running sum; returns the
+  // accumulator rescale factor.  The reference max moves only when a score
+  // passes it by more than 2^8 in weight terms (weights up to 256 are exact
+  // enough in bf16 and fp32, and O / l is unchanged by the choice of
+  // reference), so the accumulator rescale -- 128 AGPR reads, multiplies and
+  // writes -- is left for the rare large jumps instead of every new maximum.
+  auto softmax = [&](const f32x16_t& sc, int r, u32x4_t (&pk)[2]) -> float {
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sc[v]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));  // lanes l and l^32 hold one row: same decision
+    const float m_old = m_run[r];
+    const float m_new = fmaxf(m_old, tmax);
+    const bool move = !(m_new * a.scale_log2 - m_old * a.scale_log2 <= 8.f);  // also from -inf
+    const float m_ref = move ? m_new : m_old;
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    const float alpha = move ? fast_exp2((m_old - m_use) * a.scale_log2) : 1.f;
+    const float neg_m = -m_use * a.scale_log2;
+    m_run[r] = m_ref;
+    float psum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const float p0 = fast_exp2(fmaf(sc[8 * u + 2 * e2], a.scale_log2, neg_m));
+        const float p1 = fast_exp2(fmaf(sc[8 * u + 2 * e2 + 1], a.scale_log2, neg_m));
+        const uint32_t w2 = pack_bf16x2(p0, p1);
+        pk[u][e2] = w2;
+        psum = dot2_bf16(w2, kBf16PairOne, psum);  // the same rounded weights P.V uses
+      }
+    }
+    l_run[r] = l_run[r] * alpha + psum;
+    return alpha;
+  };
+  auto rescale = [&](int r, float alpha) {
+    if (__any(alpha != 1.f)) {  // no row max moved: the accumulators need no rescale
+#pragma unroll
+      for (int m = 0; m < NM; ++m) acc[r][m] *= alpha;
+    }
+  };
+  // O_r += V^T P_r^T over one key block for both row blocks; lane l of the A
+  // operand holds channel 32 m + l % 32 for keys 8 (l / 32) .. + 7 of a
+  // 16-key slice, gathered by two transposing reads (as in chunk_tile_bf16):
+  // in the 16-lane group tq, lane 4 tx + ty reads channels
+  // 32 m + 16 (tq % 2) + 4 ty .. + 3 of step row 32 kb + 16 u + 8 (tq / 2) +
+  // 4 r + tx, whose 16-byte chunk 4 m + vx sits at chunk (4 m + vx) ^ vswz(row)
+  auto load_v = [&](const unsigned char* Vs, int kb, u32x4_t (&vf)[NM][2]) {
+    uint32_t vofs = vofs0;
+    asm volatile("" : "+v"(vofs));
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const uint32_t o = vofs ^ static_cast<uint32_t>(64 * m);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const u32x2_t t2 = lds_read_tr16(Vs + (kb * 32 + 16 * u + 4 * rr) * ROW + o);
+          vf[m][u][2 * rr] = t2[0];
+          vf[m][u][2 * rr + 1] = t2[1];
+        }
+    }
+  };
+  auto pv = [&](const u32x4_t (&vf)[NM][2], const u32x4_t (&p0)[2], const u32x4_t (&p1)[2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        acc[0][m] = mfma_bf16(vf[m][u], p0[u], acc[0][m]);
+        acc[1][m] = mfma_bf16(vf[m][u], p1[u], acc[1][m]);
+      }
+  };
+  // order of a region: its 16 MFMAs, each followed by a share of the LDS
+  // reads (operands of the next region) and of the VALU work
+  auto interleave = [&](auto reads) {
+    constexpr int R = decltype(reads)::value / (2 * KS);
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+    }
+  };
+
+  // ---- the pipeline over half steps h (key block h % 2 of step h / 2).
+  // Unit h: S(h+1) = K(h+1) Q^T under the softmax of row block 1 of h, then
+  // O += V(h) P(h)^T under the softmax of row block 0 of h + 1.  Every wave
+  // runs every half step of the tile: blocks past the wave's rows are masked
+  // to nothing (m, l and O unchanged), which costs only time the wave would
+  // otherwise wait at the barrier.  Four LDS stages, step j in stage j % 4:
+  // step j's iteration reads stages j and j + 1 and loads step j + 3 into
+  // the stage step j - 1 was the last to read.
+  issue_step(0, page_ref(0), st0);
+  issue_step(BN, page_ref(BN), st1);
+  issue_step(2 * BN, page_ref(2 * BN), st2);
+  PageRef nref = page_ref(3 * BN);
+  __builtin_amdgcn_s_waitcnt(kWaitTwoSteps);  // step 0 landed
+  __syncthreads();
+  f32x16_t sa, sb;  // S of the next half step, row blocks 0 and 1
+  u32x4_t p0[2], p1[2];
+  u32x4_t kf[KS];     // K operands of the next half step
+  u32x4_t vf[NM][2];  // V^T operands of the current half step
+  load_k(st0, 0, kf);
+  qk(kf, sa, sb);
+  if (31 > H0 + wrow0) {
+    mask(0, sa, 0);
+    mask(0, sb, 1);
+  }
+  rescale(0, softmax(sa, 0, p0));
+  load_k(st0, 1, kf);
+  __builtin_amdgcn_s_waitcnt(kWaitOneStep);  // step 1 landed
+  __syncthreads();
+
+  // unit h = 2 j + kb (cur holds step j, nxt step j + 1).  Operand reads run
+  // one region ahead: region 1 reads V(h) for region 2, region 2 reads
+  // K(h+2) -- key block kb of step j + 1 -- for the next unit's region 1.
+  // An empty asm use of a region's softmax results ends the region: the
+  // compiler would otherwise sink the weights' arithmetic to their first use,
+  // past the MFMAs it is meant to run under.
+  auto pin = [](u32x4_t (&pk)[2], float& alpha) {
+    asm volatile("" : "+v"(pk[0]), "+v"(pk[1]), "+v"(alpha));
+  };
+  auto unit = [&](int h, const unsigned char* cur, const unsigned char* nxt, int kb) {
+    const f32x16_t sc = sb;  // S of half step h, row block 1
+    load_v(cur + POOL, kb, vf);
+    qk(kf, sa, sb);
+    float alpha1 = softmax(sc, 1, p1);
+    interleave(std::integral_constant<int, 4 * NM>{});
+    pin(p1, alpha1);
+    const int kn = (h + 1) * 32;  // first key of half step h + 1
+    if (kn + 31 > H0 + wrow0) {
+      mask(kn, sa, 0);
+      mask(kn, sb, 1);
+    }
+    rescale(1, alpha1);
+    u32x4_t pn[2];
+    load_k(nxt, kb, kf);
+    pv(vf, p0, p1);
+    float alpha0 = softmax(sa, 0, pn);
+    interleave(std::integral_constant<int, KS>{});
+    pin(pn, alpha0);
+    rescale(0, alpha0);
+    p0[0] = pn[0];
+    p0[1] = pn[1];
+  };
+  auto iteration = [&](int j, const unsigned char* cur, const unsigned char* nxt, unsigned char* ld) {
+    const int k0 = j * BN;
+    issue_step(k0 + 3 * BN, nref, ld);
+    unit(2 * j, cur, nxt, 0);
+    unit(2 * j + 1, cur, nxt, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    nref = page_ref(k0 + 4 * BN);
+    // step j + 2 has landed (j + 3 may still stream); after the barrier every
+    // wave's has, and stage j is free
+    __builtin_amdgcn_s_waitcnt(kWaitOneStep);
+    __syncthreads();
+  };
+  // four steps per trip, so that each step's stages are fixed objects
+  for (int j = 0; j < nsteps; j += 4) {
+    iteration(j, st0, st1, st3);
+    if (j + 1 < nsteps) iteration(j + 1, st1, st2, st0);
+    if (j + 2 < nsteps) iteration(j + 2, st2, st3, st1);
+    if (j + 3 < nsteps) iteration(j + 3, st3, st0, st2);
+  }
+  // no load may still write into LDS when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const int my_row = wrow0 + 32 * r + qc;
+    const float l_tot = l_run[r] + __shfl_xor(l_run[r], 32);  // lanes l and l^32 share a row
+    if (my_row >= Lq) continue;
+    const float inv = 1.f / l_tot;
+    bf16_t* op = static_cast<bf16_t*>(a.out) + (static_cast<size_t>(q0 + my_row) * a.num_heads + h) * D;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = m * 32 + i4 * 8 + g * 4;
+        st8(op + d, u32x2_t{pack_bf16x2(acc[r][m][4 * i4] * inv, acc[r][m][4 * i4 + 1] * inv),
+                            pack_bf16x2(acc[r][m][4 * i4 + 2] * inv, acc[r][m][4 * i4 + 3] * inv)});
+      }
+    }
+  }
+}
+
+// One workgroup per (tile, head), tiles with the most keys first (the last
+// tiles of a causal chunk); with Hq a multiple of 8 the tiles of one head all
+// run on one XCD (workgroups go to XCDs round robin), sharing its L2.
+template <int D, bool kContig>
+__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs p) {
+  using Cfg = ChunkCfg<bf16_t>::Sizes<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char st0[Cfg::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char st1[Cfg::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char st2[Cfg::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char st3[Cfg::STAGE];
+  const int b = blockIdx.x;
+  const int tile = p.ntiles - 1 - b / p.m.num_heads;
+  const int h = b - (b / p.m.num_heads) * p.m.num_heads;
+  int q0, lq, lk;
+  if (!prefill_segment<kContig>(p, q0, lq, lk)) return;
+  if (tile * kPrefillRows >= lq) return;
+  prefill_tile_bf16<D, kContig>(p.m, h, tile, q0, lq, lk, st0, st1, st2, st3);
+}
+
 // ==================================================================== launch
 namespace {
 
@@ -1965,9 +2344,55 @@ void launch_attn(const MainArgs& ma, int grid, hipStream_t st) {
   hipLaunchKernelGGL((attn_kernel<T, D, kSplit, kContig, kDefer>), dim3(grid), dim3(kThreads), 0, st, ma);
 }
 
+// A bf16 step that is one prefill chunk with at least one (256-row tile, head)
+// pair per CU: the append (hybrid_step_fwd), then prefill_kernel -- no
+// planner, no combine.  Returns false when the step is not of that kind.
+template <int D, bool kContig>
+bool run_prefill(const AttnLaunch& L, int cus, hipError_t& e) {
+  if (L.launch_mode != kLaunchFused || L.num_seqs != 1 || L.max_seqlen_q < 2) return false;
+  const long long ntiles = (static_cast<long long>(L.max_seqlen_q) + kPrefillRows - 1) / kPrefillRows;
+  const long long wgs = ntiles * L.num_heads;
+  if (wgs < cus || wgs > 0x7fffffffLL) return false;
+  if (L.append_key) {
+    e = launch_kv_append(L.append_key, L.append_value, L.slot_mapping, const_cast<void*>(L.k_cache),
+                         const_cast<void*>(L.v_cache), L.total_q, L.num_kv_heads, L.head_dim,
+                         L.num_blocks, 1, L.stream);
+    if (e != hipSuccess) return true;
+  }
+  PrefillArgs p{};
+  p.m.q = L.q;
+  p.m.kc = L.k_cache;
+  p.m.vc = L.v_cache;
+  p.m.out = L.out;
+  p.m.cu = L.cu_seqlens_q;
+  p.m.sk = L.seqlens_k;
+  p.m.bt = L.block_table;
+  p.m.num_seqs = 1;
+  p.m.num_heads = L.num_heads;
+  p.m.num_kv_heads = L.num_kv_heads;
+  p.m.group = L.num_heads / L.num_kv_heads;
+  p.m.num_blocks = L.num_blocks;
+  p.m.max_blocks = L.max_blocks;
+  p.m.scale_log2 = L.sm_scale * kLog2e;
+  p.m.cu_k = kContig ? L.cu_seqlens_k : nullptr;
+  p.total_q = L.total_q;
+  p.max_q = L.max_seqlen_q;
+  p.max_k = L.max_seqlen_k;
+  p.total_k = L.total_k;
+  p.ntiles = static_cast<int>(ntiles);
+  hipLaunchKernelGGL((prefill_kernel<D, kContig>), dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0,
+                     L.stream, p);
+  e = hipGetLastError();
+  return true;
+}
+
 template <typename T, int D, bool kContig>
 hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
   constexpr bool kF32 = sizeof(T) == 4;
+  if constexpr (!kF32) {
+    hipError_t e = hipSuccess;
+    if (run_prefill<D, kContig>(L, info.cus.load(std::memory_order_relaxed), e)) return e;
+  }
   // Chunk tiles may be split only when even the largest number of them the
   // bounds allow (tiles_cap per head) fills at most half of split_items; every
   // other step runs the instance without the split code.

@@ -121,6 +121,91 @@ def test_chunk_split(case):
     G.compare(G.to_f64(out2), ref, dt, f"split case {case}, second call")
 
 
+# ---------------------------------------------------------------- one-segment prefill kernel
+# A bf16 step that is one prefill chunk, with at least one (256-row tile, head)
+# pair per CU, runs a kernel of its own (64 query rows per wave, one workgroup
+# per CU): no planner, no combine, and the workspace is left untouched, which
+# is how the tests see which path ran.  Ragged last tiles, histories off the
+# page and key-step grid, GQA, D = 64 and 128.
+PREFILL_CASES = [
+    # (segments (Lq, Lk), Hq, Hkv, D, dtype, seed)
+    ([(1000, 1000)], 64, 64, 128, W.BF16, 41),
+    ([(777, 3000)], 64, 8, 128, W.BF16, 42),      # GQA 8, history 2223
+    ([(300, 300)], 128, 128, 64, W.BF16, 43),
+    ([(513, 530)], 128, 128, 128, W.BF16, 44),    # one row in the last tile, history 17
+    ([(1000, 1000)], 32, 32, 128, W.BF16, 45),    # 4 x 32 pairs: below one per CU, fused path
+]
+_SENTINEL = 0x5A
+
+
+def _prefill_expected(meta, hq, dt):
+    """Whether the step takes the one-segment prefill kernel on this device."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = -(-int(meta.max_seqlen_q) // 256)
+    return dt == W.BF16 and meta.num_seqs == 1 and meta.max_seqlen_q > 1 and tiles * hq >= cus
+
+
+def _marked_workspace(meta, hq, d):
+    ws = B.alloc_workspace(meta.num_seqs, meta.total_q, meta.max_seqlen_k, hq, d)
+    ws.fill_(_SENTINEL)
+    return ws
+
+
+def _workspace_untouched(ws):
+    return bool((ws[:256] == _SENTINEL).all().item())
+
+
+@pytest.mark.parametrize("case", range(len(PREFILL_CASES)))
+def test_one_segment_prefill(case):
+    import torch
+    segs, hq, hkv, d, dt, seed = PREFILL_CASES[case]
+    spec, meta = W.custom_step(segs, hq, hkv, d, dt, seed=seed)
+    hs = W.host_values(spec, meta, seed=seed)
+    ds = _dev(hs)
+    ref, kc_ref, vc_ref = G.oracle_full(ds, hs.k_cache, hs.v_cache)
+    wide = _prefill_expected(meta, hq, dt)
+    G.note(f"one-segment prefill case={case} segs={segs} H={hq}/{hkv} D={d} prefill kernel={wide}")
+    ws = _marked_workspace(meta, hq, d)
+    out = G.gpu_step(ds, workspace=ws)
+    assert _workspace_untouched(ws) == wide
+    kc, vc = G.host_pools(ds)
+    assert kc.tobytes() == kc_ref.tobytes() and vc.tobytes() == vc_ref.tobytes()
+    G.compare(G.to_f64(out), ref, dt, f"prefill case {case}")
+    # the same step through hybrid_step_fwd (append inside) and through the
+    # packed-K/V entry point: byte-identical
+    ds_b = _dev(hs)
+    ws_b = _marked_workspace(meta, hq, d)
+    out_b = _step(ds_b, ws_b)
+    assert _workspace_untouched(ws_b) == wide
+    assert torch.equal(out_b.view(torch.uint8), out.view(torch.uint8))
+    k, v, cu_k = G.contiguous_kv(ds)
+    out_c = B.varlen_attn_fwd(ds.q, k, v, ds.cu_seqlens_q, cu_k, meta.max_seqlen_q, meta.max_seqlen_k)
+    torch.cuda.synchronize()
+    assert torch.equal(out_c.view(torch.uint8), out.view(torch.uint8))
+
+
+def test_one_segment_prefill_declared_max_above_rows():
+    """max_seqlen_q is an upper bound (at most max_seqlen_k): tiles past the
+    segment's rows do nothing."""
+    import torch
+    spec, meta = W.custom_step([(700, 1500)], 64, 64, 128, W.BF16, seed=46)
+    hs = W.host_values(spec, meta, seed=46)
+    ds = _dev(hs)
+    ref, _, _ = G.oracle_full(ds, hs.k_cache, hs.v_cache)
+    G.note("one-segment prefill: 700 rows, max_seqlen_q 1280")
+    B.paged_kv_append(ds.key, ds.value, ds.slot_mapping, ds.k_cache, ds.v_cache)
+    ws = _marked_workspace(meta, 64, 128)
+    out = torch.full_like(ds.q, float("nan"))
+    B.hybrid_attn_fwd(ds.q, ds.k_cache, ds.v_cache, ds.cu_seqlens_q, ds.seqlens_k, ds.block_table,
+                      1280, meta.max_seqlen_k, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert _workspace_untouched(ws) == _prefill_expected(W.StepMeta(
+        meta.cu_seqlens_q, meta.seqlens_k, meta.block_table, None, meta.num_blocks,
+        meta.page_size, 1280, meta.max_seqlen_k), 64, W.BF16)
+    G.compare(G.to_f64(out), ref, W.BF16, "prefill, declared max above the rows")
+
+
 # ---------------------------------------------------------------- two-launch baseline
 # The chunk role and the decode role in separate launches (back to back, or on
 # two streams): the same plan and items as the fused launch, so the output is
