@@ -1,8 +1,17 @@
-// Token-budget step generator (declared in include/ha_scheduler.h): running
-// requests first in admission order, then waiting requests while budget is
-// left; each takes min(remaining tokens, threshold, budget left).  Host code
-// only.  Source: wangyu.me chunked-prefill page, section on the vLLM
-// implementation (token budget, running-first scheduler, metadata assembly).
+// Token-budget step generator (declared in include/ha_scheduler.h).  Host
+// code only.  The rules, as the wangyu.me chunked-prefill page states them in
+// its section on the vLLM implementation (token budget, running-first
+// scheduling, metadata assembly):
+//   * a step carries at most max_num_batched_tokens tokens;
+//   * requests already running are served before new ones, in the order they
+//     were admitted; waiting requests are admitted in arrival order while
+//     budget is left;
+//   * a request is granted the tokens it still has to put through the model
+//     (its prompt, or the rest of it, or one token while decoding), cut to
+//     the long-prefill threshold and to the budget left -- a long prompt thus
+//     runs as several chunks.
+// Added here: a grant is also cut to the KV pages the pool can still hand out
+// (no preemption), and a per-step segment cap.
 #include "ha_scheduler.h"
 
 #include <algorithm>
@@ -51,11 +60,26 @@ struct ha_sched {
     for (Request* r : running) delete r;
   }
 
-  // Tokens (up to want) request r can take this step given the free pages.
-  int32_t fit(const Request& r, int32_t want) const {
-    const int64_t have = static_cast<int64_t>(r.pages.size()) * kPageTokens - r.computed;
-    const int64_t room = have + static_cast<int64_t>(free_pages.size()) * kPageTokens;
-    return static_cast<int32_t>(std::min<int64_t>(want, std::max<int64_t>(room, 0)));
+  // Tokens request r is granted this step (0: none): what it still has to
+  // compute -- its known tokens (prompt plus samples) not yet through the
+  // model -- cut to the long-prefill threshold, to the budget left and to
+  // the room its pages plus the free pages leave.
+  int32_t grant(const Request& r, int32_t left) const {
+    int64_t n = r.known() - r.computed;
+    if (threshold > 0) n = std::min<int64_t>(n, threshold);
+    n = std::min<int64_t>(n, left);
+    const int64_t room = static_cast<int64_t>(r.pages.size() + free_pages.size()) * kPageTokens - r.computed;
+    return static_cast<int32_t>(std::max<int64_t>(std::min(n, room), 0));
+  }
+
+  // Plans request r's grant for this step; false when it gets nothing.
+  bool take(Request& r, int32_t& left) {
+    const int32_t n = grant(r, left);
+    if (n <= 0) return false;
+    grow(r, r.computed + n);
+    planned.push_back({&r, r.computed, n});
+    left -= n;
+    return true;
   }
 
   void grow(Request& r, int32_t upto_tokens) {
@@ -116,30 +140,16 @@ ha_status ha_sched_next_step(ha_sched* s, ha_step_shape* shape, int32_t* cu_seql
     return HA_ERR_INVALID_ARGUMENT;
   s->planned.clear();
   int32_t left = s->budget;
-  auto cap = [&](int32_t n) {
-    if (s->threshold > 0) n = std::min(n, s->threshold);
-    return std::min(n, left);
-  };
-  // running requests first, in admission order
   const size_t seg_cap = static_cast<size_t>(max_seqs);
-  for (Request* r : s->running) {
-    if (left == 0 || s->planned.size() == seg_cap) break;
-    const int32_t n = s->fit(*r, cap(r->known() - r->computed));
-    if (n <= 0) continue;
-    s->grow(*r, r->computed + n);
-    s->planned.push_back({r, r->computed, n});
-    left -= n;
-  }
-  // then the waiting queue fills what is left
-  while (left > 0 && !s->waiting.empty() && s->planned.size() < seg_cap) {
-    Request* r = s->waiting.front();
-    const int32_t n = s->fit(*r, cap(r->prompt));
-    if (n <= 0) break;  // the pool is full: the queue waits
+  auto open = [&] { return left > 0 && s->planned.size() < seg_cap; };
+  // the running requests, in admission order; one the pool cannot serve now
+  // (no page left) skips this step
+  for (size_t i = 0; i < s->running.size() && open(); ++i) s->take(*s->running[i], left);
+  // then admissions from the waiting queue, in arrival order; when the head of
+  // the queue cannot be served the queue waits
+  while (open() && !s->waiting.empty() && s->take(*s->waiting.front(), left)) {
+    s->running.push_back(s->waiting.front());
     s->waiting.pop_front();
-    s->running.push_back(r);
-    s->grow(*r, n);
-    s->planned.push_back({r, 0, n});
-    left -= n;
   }
   ha_step_shape sh{};
   if (s->planned.empty()) {
