@@ -179,10 +179,45 @@ def test_one_segment_prefill(case):
     out_b = _step(ds_b, ws_b)
     assert _workspace_untouched(ws_b) == wide
     assert torch.equal(out_b.view(torch.uint8), out.view(torch.uint8))
+    kc_b, vc_b = G.host_pools(ds_b)
+    assert kc_b.tobytes() == kc.tobytes() and vc_b.tobytes() == vc.tobytes()
     k, v, cu_k = G.contiguous_kv(ds)
     out_c = B.varlen_attn_fwd(ds.q, k, v, ds.cu_seqlens_q, cu_k, meta.max_seqlen_q, meta.max_seqlen_k)
     torch.cuda.synchronize()
     assert torch.equal(out_c.view(torch.uint8), out.view(torch.uint8))
+
+
+def test_one_segment_prefill_appends_tokens_outside_the_segment():
+    """hybrid_step_fwd on a one-segment step whose token list also holds rows
+    past the segment (a padding token, and tokens bound for unused slots):
+    every token with a valid slot is appended, as paged_kv_append does, and
+    the segment's output is unchanged."""
+    import torch
+    spec, meta = W.custom_step([(1000, 1000)], 64, 64, 128, W.BF16, seed=47)
+    hs = W.host_values(spec, meta, seed=47)
+    ds = _dev(hs)
+    extra = 6
+    rng = np.random.default_rng(47)
+    free = np.setdiff1d(meta.poison_slots, meta.slot_mapping)  # slots no segment owns or appends to
+    slots = np.concatenate([meta.slot_mapping, [-1], rng.choice(free, extra - 1, replace=False)])
+    g = torch.Generator(device="cuda")
+    g.manual_seed(48)
+    pad = lambda x: torch.cat([x, torch.randn((extra,) + tuple(x.shape[1:]), generator=g, device="cuda").to(x.dtype)])
+    ds2 = W.DeviceStep(spec, meta, pad(ds.q), pad(ds.key), pad(ds.value), ds.k_cache.clone(), ds.v_cache.clone(),
+                       ds.cu_seqlens_q, ds.seqlens_k, ds.block_table,
+                       torch.from_numpy(slots.astype(np.int32)).cuda())
+    G.note("one-segment prefill: 6 tokens past the segment")
+    ref_k, ref_v = ds.k_cache.clone(), ds.v_cache.clone()
+    B.paged_kv_append(ds2.key, ds2.value, ds2.slot_mapping, ref_k, ref_v)
+    out = torch.empty_like(ds2.q)
+    B.hybrid_step_fwd(ds2.key, ds2.value, ds2.slot_mapping, ds2.q, ds2.k_cache, ds2.v_cache,
+                      ds2.cu_seqlens_q, ds2.seqlens_k, ds2.block_table, meta.max_seqlen_q,
+                      meta.max_seqlen_k, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(ds2.k_cache.view(torch.int16), ref_k.view(torch.int16))
+    assert torch.equal(ds2.v_cache.view(torch.int16), ref_v.view(torch.int16))
+    ref_out = G.gpu_step(ds)
+    assert torch.equal(out[:1000].view(torch.uint8), ref_out.view(torch.uint8))
 
 
 def test_one_segment_prefill_declared_max_above_rows():
