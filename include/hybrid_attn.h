@@ -218,7 +218,11 @@ ha_status hybrid_step_fwd_noalloc(const void* key, const void* value, const int3
  * launches instead of one fused launch: the "separate prefill and decode
  * kernels" alternative the kwkr.cn hybrid-attention article argues against
  * (section on the hybrid batch).  It exists as a comparison baseline; results
- * are bitwise equal to hybrid_attn_fwd for the same inputs and workspace size.
+ * are bitwise equal to hybrid_attn_fwd for the same inputs and workspace size,
+ * except for bf16 steps of a single segment with at least one (256-row tile,
+ * head) pair per compute unit: hybrid_attn_fwd runs those through a kernel
+ * of their own (no decode work to share the GPU with), whose rounding differs
+ * within the stated tolerance.
  *
  *   two_streams = 0  chunk launch, then decode launch, on `stream`
  *   two_streams != 0 the chunk launch runs on a second stream the library
