@@ -1921,11 +1921,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(MainArgs a) {
 // each wave owns 64 query rows (two 32-row blocks that share every K and V
 // operand read, so a step's LDS reads serve twice the MFMA work of the fused
 // kernel's 32-row waves), a tile is 256 rows x one head, a workgroup holds a
-// whole CU (one wave per SIMD, up to 512 registers: the O accumulators go to
-// AGPRs) and four LDS stages keep K/V loads two steps ahead.  With one wave
-// per SIMD nothing else hides the softmax, so the step is software pipelined:
-// each block's softmax is scheduled among MFMAs of the other phase.  Same data
-// layout, swizzles, masks and online softmax as chunk_tile_bf16.
+// whole CU (one wave per SIMD: 256 VGPRs, with AGPRs as spill space) and four
+// LDS stages keep K/V loads two steps ahead.  With one wave per SIMD nothing
+// else hides the softmax, so the key loop is software pipelined: each row
+// block's softmax is scheduled among the MFMAs of the other phase.  Same data
+// layout, swizzles and masks as chunk_tile_bf16; the softmax moves its
+// reference max lazily (see below).
 constexpr int kPrefillBlocks = 2;                          // 32-row blocks per wave
 constexpr int kPrefillRows = 4 * 32 * kPrefillBlocks;      // query rows per tile
 
@@ -2091,8 +2092,9 @@ __device__ void prefill_tile_bf16(const MainArgs& a, int h, int tile, int q0, in
   // accumulator rescale factor.  The reference max moves only when a score
   // passes it by more than 2^8 in weight terms (weights up to 256 are exact
   // enough in bf16 and fp32, and O / l is unchanged by the choice of
-  // reference), so the accumulator rescale -- 128 AGPR reads, multiplies and
-  // writes -- is left for the rare large jumps instead of every new maximum.
+  // reference), so the accumulator rescale -- 64 multiplies per row block,
+  // behind a branch -- is left for the rare large jumps instead of every new
+  // maximum (on N(0,1) data a wave saw one in about three half steps).
   auto softmax = [&](const f32x16_t& sc, int r, u32x4_t (&pk)[2]) -> float {
     float tmax = -INFINITY;
 #pragma unroll
