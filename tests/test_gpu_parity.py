@@ -187,6 +187,27 @@ def test_one_segment_prefill(case):
     assert torch.equal(out_c.view(torch.uint8), out.view(torch.uint8))
 
 
+@pytest.mark.parametrize("case", [1, 3, 4])
+def test_one_segment_prefill_packed_keys_at_an_offset(case):
+    """varlen_attn_fwd on one segment whose keys start past row 0 of the packed
+    buffers (NaN rows before and after them): byte-identical to the paged call."""
+    import torch
+    segs, hq, hkv, d, dt, seed = PREFILL_CASES[case]
+    spec, meta = W.custom_step(segs, hq, hkv, d, dt, seed=seed)
+    ds = _dev(W.host_values(spec, meta, seed=seed))
+    G.note(f"one-segment prefill, packed keys at row 37: case={case} segs={segs}")
+    paged = G.gpu_step(ds)
+    k, v, cu_k = G.contiguous_kv(ds)
+    lead = torch.full((37,) + tuple(k.shape[1:]), float("nan"), dtype=k.dtype, device=k.device)
+    k2, v2 = torch.cat([lead, k]).contiguous(), torch.cat([lead, v]).contiguous()
+    ws = _marked_workspace(meta, hq, d)
+    out = B.varlen_attn_fwd(ds.q, k2, v2, ds.cu_seqlens_q, cu_k + 37, meta.max_seqlen_q,
+                            meta.max_seqlen_k, workspace=ws)
+    torch.cuda.synchronize()
+    assert _workspace_untouched(ws) == _prefill_expected(meta, hq, dt)
+    assert torch.equal(out.view(torch.uint8), paged.view(torch.uint8))
+
+
 def test_one_segment_prefill_appends_tokens_outside_the_segment():
     """hybrid_step_fwd on a one-segment step whose token list also holds rows
     past the segment (a padding token, and tokens bound for unused slots):

@@ -1,6 +1,6 @@
 """hybrid_step_fwd_noalloc (the library's own device scratch array as the
 workspace, no allocation in the call) against hybrid_step_fwd with a
-caller-allocated workspace, through the C ABI: three calls in a row on
+caller-allocated workspace, through the C ABI: four calls in a row on
 shrinking inputs.  Pools byte-identical; outputs within the oracle's bf16 /
 fp32 tolerance of the workspace call's, and byte-identical where that call's
 workspace fits the 64 MiB array (same plan, same kernels)."""
@@ -17,14 +17,16 @@ SCRATCH_BYTES = 64 << 20
 
 
 def _steps():
-    """(name, spec, meta, host step or None): the mixed workload (its usual
-    workspace is larger than the scratch array: capped layout), the worked
-    example (fp32, split chunk tiles: chunk partials in the array), a small
-    step."""
+    """(name, spec, meta, host step or None): a one-segment bf16 prefill (the
+    path that uses no workspace), the mixed workload (its usual workspace is
+    larger than the scratch array: capped layout), the worked example (fp32,
+    split chunk tiles: chunk partials in the array), a small step."""
+    spec0, meta0 = W.custom_step([(1000, 1500)], 64, 64, 128, W.BF16, seed=6)
     spec2, meta2 = W.make_step(2)
     spec1, meta1 = W.make_step(1)
     spec3, meta3 = W.custom_step([(1, 300), (70, 500), (1, 40)], 4, 4, 128, W.BF16, seed=5)
-    return [("mixed", spec2, meta2, None), ("worked example", spec1, meta1, W.host_values(spec1, meta1)),
+    return [("one-segment prefill", spec0, meta0, None), ("mixed", spec2, meta2, None),
+            ("worked example", spec1, meta1, W.host_values(spec1, meta1)),
             ("small", spec3, meta3, W.host_values(spec3, meta3, seed=5))]
 
 
