@@ -159,13 +159,14 @@ __device__ __forceinline__ void plan_small(const PlanArgs& a) {  // the 64 lanes
     }
   }
   const bool bad = b < a.num_seqs && lq < 0;
-  // decode split: the smallest candidate whose items and partial slots fit
+  // decode split: the smallest candidate whose whole splits stay within the
+  // item target and whose partial slots (tail pieces counted) fit
   int pick = kSplitCandidates - 1;
   for (int k = 0; k < kSplitCandidates; ++k) {
     const int sh = kSplitMinLog2 + k;
     long long full = 0, tail = 0;
     if (lq == 1) decode_pieces(lk, sh, full, tail);
-    long long items = full + tail, parts = items > 1 ? items : 0;
+    long long items = lq == 1 ? (lk + (1LL << sh) - 1) >> sh : 0, parts = full + tail > 1 ? full + tail : 0;
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) {
       items += __shfl_xor(items, m);
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         if (lq == 1) {
           long long full, tail;
           decode_pieces(lk, sh, full, tail);
-          items += full + tail;
+          items += (lk + (1LL << sh) - 1) >> sh;  // whole splits: the item target ignores tail pieces
           parts += full + tail > 1 ? full + tail : 0;
           dkeys += lk;
         } else if (lq >= 2) {
@@ -352,7 +353,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __syncthreads();
   // Wave 0 totals the groups: lanes 0..31 one candidate each, lanes 32..35 the
   // chunk statistics; the split is the smallest candidate that fits the
-  // partial slots and keeps the decode item count near the target (the largest
+  // partial slots and keeps the decode whole-split count near the target (the largest
   // candidate, 2^30 keys, always fits).
   if (tid < kWave) {
     long long items = 0, parts = 0, stat = 0;
@@ -1524,9 +1525,11 @@ __device__ __forceinline__ int find_segment_lds(const int* prefix, int n, int x)
 
 // kSplit: this launch may meet split chunk tiles (the planner was allowed to
 // split); the instance without it keeps the unsplit roles' register allocation.
-// kDefer: a chunk item claims its successor only when it is done (else at its
-// start, hiding the atomic's latency).  Chosen by the host per step, so that
-// the steps that do not need it keep the instance tuned without it.
+// kDefer: a chunk item, or a decode item of at least kLateClaimKeys keys, claims
+// its successor only when it is done; other items claim it at their start,
+// which hides the atomic's latency behind the item.  An item reserved at the
+// start of a long one waits behind it while other workgroups run out of work,
+// so long items reserve nothing.
 template <typename T, int D, bool kSplit, bool kContig, bool kDefer>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
   constexpr int kSmem = ChunkCfg<T>::template Sizes<D>::BYTES;
@@ -1751,10 +1754,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(MainArgs a) {
     __syncthreads();
     if (kind == 0) break;
     // the next item, claimed while this one runs (hides the atomic's latency),
-    // or with kDefer, after a chunk item only once it is done: an item
-    // reserved at the start of a long chunk tile waits behind it while other
-    // workgroups run dry
-    if (threadIdx.x == 0) s_next = (kDefer && kind == 1) ? kPending : claim();
+    // or with kDefer, after a chunk item or a long decode item only once it is
+    // done: an item reserved at the start of a long item waits behind it while
+    // other workgroups run dry
+    if (threadIdx.x == 0) s_next = (kDefer && (kind == 1 || p3 >= kLateClaimKeys)) ? kPending : claim();
     if (kind == 1) {
       if (csplit == 1) {
         if constexpr (sizeof(T) == 2) chunk_tile_bf16<D, false, kContig, kDefer>(a, seg, p1, p2, 0, 1, smem, smem_b);
@@ -2486,18 +2489,15 @@ hipError_t run(const AttnLaunch& L, DeviceInfo& info, int dev, int dt, int di) {
               tile_prefix, dec_prefix, part_prefix, tail_prefix,
               reinterpret_cast<float*>(ws + L.ws.partials),
               reinterpret_cast<float*>(ws + L.ws.chunk_partials), L.cu_seqlens_k, 3, half};
-  // Deferred chunk claims (kDefer): always for fp32; for bf16 when the longest
-  // chunk alone has more tiles than the grid has workgroups, so that chunk-first
-  // workgroups run several chunk items each and an early claim would reserve
-  // a chunk item behind a chunk item (a 1984-token chunk + 64 decodes, 64
-  // heads: 3157 -> 3035 us).  In the other bf16 steps chunk-first workgroups
-  // reserve decode items, and the instance without it is faster (two 512-token
-  // chunks + 30 decodes, 32 heads: by 3.5 us).
-  const bool defer = kF32 || static_cast<long long>((L.max_seqlen_q + kChunkRows - 1) / kChunkRows) *
-                                     L.num_heads > grid;
-  auto attn = split_ok ? launch_attn<T, D, true, kContig, kF32>
-                       : (defer ? launch_attn<T, D, false, kContig, true>
-                                : launch_attn<T, D, false, kContig, kF32>);
+  // Unsplit steps run the instance with deferred claims (kDefer): a chunk item,
+  // or a long decode item, does not reserve its successor while it runs.  With
+  // early claims a 1984-token chunk + 64 decodes (64 heads) ran 3157 us against
+  // 3035 (chunk items reserved behind chunk items), and the steps with long
+  // decode histories ended on workgroups that had reserved a full split behind
+  // a full split (130K-token chunk + 64 decodes, 256 decodes of up to 32K
+  // keys: 0.6-0.8 % slower); the two-chunk mixed step measures the same
+  // either way.  The split instance keeps early claims for bf16.
+  auto attn = split_ok ? launch_attn<T, D, true, kContig, kF32> : launch_attn<T, D, false, kContig, true>;
   if (L.launch_mode == kLaunchFused) {
     attn(ma, grid, L.stream);
   } else {

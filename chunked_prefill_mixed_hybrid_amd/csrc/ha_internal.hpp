@@ -18,7 +18,7 @@ constexpr int kSplitMinLog2 = 8;
 constexpr int kSplitMin = 1 << kSplitMinLog2;  // smallest decode KV split, in keys
 constexpr int kSplitCandidates = 23;  // decode split sizes kSplitMin << k, k < 23 (up to 2^30)
 constexpr int kPartsMax = 16384;    // cap on (segment, split) partial slots
-constexpr int kItemsPerSlot = 16;   // decode work items aimed at per resident workgroup
+constexpr int kItemsPerSlot = 16;   // decode splits aimed at per resident workgroup (tail pieces not counted)
 constexpr int kHeadsPerDecodeItem = 4;  // bf16: one head per 16-lane row of every wave; fp32: one per wave
 constexpr int kMaxSeqlenK = 1 << 30;
 // Decode tail: when the decode split is at least 2^kTailMinLog2 keys, each
@@ -27,6 +27,9 @@ constexpr int kMaxSeqlenK = 1 << 30;
 // of full ones (fewer workgroups idle while the last items finish).
 constexpr int kTailMinLog2 = 11;
 constexpr int kTailLog2 = 2;
+// Decode items of at least this many keys claim their successor only when they
+// are done (in the instance with deferred claims), as chunk items do.
+constexpr int kLateClaimKeys = 1 << kTailMinLog2;
 // Full splits and tail pieces of a decode segment of lk keys at split 2^sh.
 __host__ __device__ inline void decode_pieces(long long lk, int sh, long long& full, long long& tail) {
   const long long n = (lk + (1LL << sh) - 1) >> sh;
