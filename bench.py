@@ -9,10 +9,11 @@ is the largest single-GPU step: a chunk of 1024 tokens at history 130048 of a
 131072-token prompt plus 64 decodes with history U[8192, 131072], 32 heads x
 128, bf16, 16-token pages, shuffled block ids (75 GB of pages).
 
-Timed region: K steps on one stream, each preceded by a 1 GiB write that
+Timed region: K steps on one stream, each preceded by a 1 GiB read that
 evicts L2 and the 256 MB MALL (cold, as a serving step meets its KV), each
 bracketed by HIP events; `value` is the median step in microseconds.  Also
-reported: the same steps back to back (warm), the fraction of the step roofline
+reported: the same steps back to back (warm), the same steps after a 1 GiB
+write instead (whose dirty lines are written back during the step), the fraction of the step roofline
 max(FLOPs / MFMA peak, bytes / HBM peak), a roofline object for the attention
 call (HIP events on the stream its kernels run on), the CPU oracle's time on
 the host cores as a baseline (a bounded sample of the step, scaled by the
@@ -230,9 +231,33 @@ class Runner:
         self.torch.cuda.empty_cache()
 
 
-def timed_steps(r: Runner, steps, flush_buf):
+class Flush:
+    """Cache eviction before a timed step, on the step's stream.  "read" sums a
+    1 GiB buffer into one float: every XCD's L2 and the MALL are refilled with
+    the buffer, so the step meets its inputs in HBM, and nothing dirty is left
+    behind.  "write" fills a 1 GiB buffer: the same eviction, but it leaves up
+    to the MALL's and the L2s' capacity of dirty lines, whose write-back to HBM
+    then runs during the timed step and is charged to it."""
+
+    def __init__(self, torch, kind):
+        self.torch, self.kind = torch, kind
+        if kind == "read":
+            self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+            self.acc = torch.zeros((), dtype=torch.float32, device="cuda")
+        else:
+            self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+
+    def __call__(self, stream):
+        with self.torch.cuda.stream(stream):
+            if self.kind == "read":
+                self.torch.sum(self.buf, dim=(0,), out=self.acc)
+            else:
+                self.buf.fill_(1)
+
+
+def timed_steps(r: Runner, steps, flush):
     """Per-step durations (ms, HIP events on r.stream) of `steps` steps, each
-    preceded by a write of flush_buf when it is given; and the wall time of
+    preceded by flush(r.stream) when a flush is given; and the wall time of
     the whole loop, bracketed by device synchronisation."""
     torch = r.torch
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -240,9 +265,8 @@ def timed_steps(r: Runner, steps, flush_buf):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for e0, e1 in ev:
-        if flush_buf is not None:
-            with torch.cuda.stream(r.stream):
-                flush_buf.fill_(1)
+        if flush is not None:
+            flush(r.stream)
         e0.record(r.stream)
         r.step()
         e1.record(r.stream)
@@ -251,15 +275,14 @@ def timed_steps(r: Runner, steps, flush_buf):
     return np.array([e0.elapsed_time(e1) for e0, e1 in ev]), wall
 
 
-def timed_calls(r: Runner, steps, flush_buf):
+def timed_calls(r: Runner, steps, flush):
     """Durations (ms) of the append and of the attention call, as two
     separate calls per step (each step preceded by the flush when given)."""
     torch = r.torch
     ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
     for e0, e1, e2 in ev:
-        if flush_buf is not None:
-            with torch.cuda.stream(r.stream):
-                flush_buf.fill_(1)
+        if flush is not None:
+            flush(r.stream)
         e0.record(r.stream)
         r.append()
         e1.record(r.stream)
@@ -275,21 +298,29 @@ def percentiles(ms):
     return {f"p{q}": round(float(np.percentile(ms, q)) * 1e3, 2) for q in (10, 50, 90)}
 
 
-def measure(r: Runner, steps, warmup, flush_buf):
+def measure(r: Runner, steps, warmup, flushes):
+    """flushes: {"read": Flush, "write": Flush}, or None for no flush at all."""
     torch = r.torch
     with torch.cuda.stream(r.stream):
         for _ in range(warmup):
             r.step()
     torch.cuda.synchronize()
-    cold_ms, cold_wall = timed_steps(r, steps, flush_buf)
+    flush = flushes["read"] if flushes else None
+    cold_ms, cold_wall = timed_steps(r, steps, flush)
     warm_ms, warm_wall = timed_steps(r, steps, None)
-    append_ms, attn_ms = timed_calls(r, steps, flush_buf)
+    append_ms, attn_ms = timed_calls(r, steps, flush)
+    wflush_ms = timed_steps(r, steps, flushes["write"])[0] if flushes else None
     w = algorithmic_work(r.meta, r.spec)
     roof_us, bound = step_roofline_us(w, r.spec)
     cold_us = float(np.median(cold_ms)) * 1e3
     return {"w": w, "roof_us": roof_us, "bound": bound, "cold_ms": cold_ms, "cold_us": cold_us,
             "cold_wall": cold_wall, "warm_ms": warm_ms, "warm_wall": warm_wall,
-            "append_ms": append_ms, "attn_ms": attn_ms}
+            "append_ms": append_ms, "attn_ms": attn_ms, "wflush_ms": wflush_ms}
+
+
+def write_flush_us(m):
+    """Median step after the write flush (us), or None when no flush ran."""
+    return None if m["wflush_ms"] is None else round(float(np.median(m["wflush_ms"])) * 1e3, 2)
 
 
 def summary(r: Runner, m) -> dict:
@@ -297,6 +328,7 @@ def summary(r: Runner, m) -> dict:
     attn_us = float(np.mean(m["attn_ms"])) * 1e3
     return {"cold_us_per_step": round(m["cold_us"], 2),
             "warm_us_per_step": round(1e3 * float(np.median(m["warm_ms"])), 2),
+            "after_write_flush_us_per_step": write_flush_us(m),
             "step_roofline_us": round(m["roof_us"], 2), "bound": m["bound"],
             "frac_step_roofline": round(m["roof_us"] / m["cold_us"], 4),
             "attn_us": round(attn_us, 2),
@@ -315,7 +347,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true",
-                    help="skip the 1 GiB cache-flush write before each timed step")
+                    help="skip the 1 GiB cache flush before each timed step")
     ap.add_argument("--launch", default="fused", choices=["fused", "serial", "two-streams"],
                     help="fused: hybrid_attn_fwd; serial / two-streams: the two-launch baseline")
     ap.add_argument("--entry", default="step", choices=["step", "calls"],
@@ -335,13 +367,13 @@ def main():
     B.load()  # fail loudly if the HIP library is missing
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
-    flush_buf = None if args.no_flush else torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    flushes = None if args.no_flush else {"read": Flush(torch, "read"), "write": Flush(torch, "write")}
 
     r = Runner(args.config, args.seed, args.launch, args.entry, stream)
     spec, meta = r.spec, r.meta
     print(f"[bench] {spec.name}: {meta.num_seqs} segments, {meta.total_q} rows", file=sys.stderr,
           flush=True)
-    m = measure(r, args.steps, args.warmup, flush_buf)
+    m = measure(r, args.steps, args.warmup, flushes)
     w = m["w"]
     us_step = m["cold_us"]
     peak_tf = PEAK_MFMA_TFLOPS[spec.dtype]
@@ -380,10 +412,12 @@ def main():
                    "max_seqlen_q": meta.max_seqlen_q, "max_seqlen_k": meta.max_seqlen_k,
                    "seed": args.seed, "launch": args.launch,
                    "entry": "hybrid_step_fwd" if r.one_call else "paged_kv_append + attention",
-                   "timing": ("median of per-step HIP events, each step after a 1 GiB cache flush"
-                              if flush_buf is not None else "median of per-step HIP events, no flush")},
+                   "timing": ("median of per-step HIP events, each step after a 1 GiB read that "
+                              "evicts L2 and the MALL" if flushes else
+                              "median of per-step HIP events, no flush")},
         "timed_region_s": round(m["cold_wall"], 4),
         "warm_us_per_step": round(1e6 * m["warm_wall"] / args.steps, 2),
+        "after_write_flush_us_per_step": write_flush_us(m),
         "tflops": round(w["flops"] / (us_step * 1e-6) / 1e12, 2),
         "kv_gbps": round(w["kv_bytes"] / (us_step * 1e-6) / 1e9, 1),
         "step_gbps": round(w["step_bytes"] / (us_step * 1e-6) / 1e9, 1),
@@ -412,7 +446,7 @@ def main():
     for c in [c for c in args.extra.split(",") if c and c != args.config]:
         rx = Runner(c, args.seed, args.launch, args.entry, stream)
         print(f"[bench] extra workload {rx.spec.name}", file=sys.stderr, flush=True)
-        extras[rx.spec.name] = summary(rx, measure(rx, args.steps, args.warmup, flush_buf))
+        extras[rx.spec.name] = summary(rx, measure(rx, args.steps, args.warmup, flushes))
         rx.free()
     if extras:
         result["workloads"] = extras
