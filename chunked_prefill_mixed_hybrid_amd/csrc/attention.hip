@@ -519,6 +519,9 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // ... and the one that waits until at most n vector memory loads are
 // outstanding (vmcnt is split: bits 3:0 and 15:14)
 constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+// ... and the one that waits for LDS (and scalar memory) operations only:
+// vmcnt 63, expcnt 7, lgkmcnt 0
+constexpr int kWaitLgkmcnt0 = 0xC07F;
 
 constexpr uint32_t kBf16PairOne = 0x3f803f80u;  // (1.0, 1.0) as a bf16 pair
 
@@ -1918,6 +1921,45 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(MainArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- prefill helpers
+// Pool-to-LDS 16-byte load (as load_lds16) written as inline asm, so that the
+// compiler does not see it write LDS: with dozens of these in flight its alias
+// tracking of such loads runs out of slots, and it then waits for all of them
+// in front of LDS reads of other stages.  The caller waits (vmcnt) for the
+// loads it needs; the instruction has no register result.
+__device__ __forceinline__ void load_lds16_async(__amdgpu_buffer_rsrc_t rsrc, unsigned char* dst, uint32_t off) {
+  const auto lp = (__attribute__((address_space(3))) unsigned char*)dst;
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lp)));
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(off), "s"(rsrc), "{m0}"(lds) : "memory");
+}
+// Lanes l and l ^ 32 combined with one VALU lane swap (v_permlane32_swap)
+// instead of an LDS permute, whose result would wait behind every LDS read
+// issued before it.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Workgroup barrier that leaves the pool-to-LDS loads in flight.  A
+// __syncthreads() fences LDS at workgroup scope, and since those loads write
+// LDS it waits for every one of them, including the steps loaded ahead.  Here
+// each wave only finishes its own LDS reads (a stage is overwritten after the
+// barrier that follows its last read) and the caller waits (vmcnt) for the
+// loads of the steps it needs.  The empty asm statements keep the compiler
+// from moving LDS accesses across the barrier, the scheduling barriers keep
+// every other instruction (the MFMAs above all) on its side of it.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ==================================================================== one-segment prefill, bf16
 // A step that is a single prefill chunk (one segment) has no decode work to
 // share the CUs with, so it runs a kernel shaped for the matrix cores alone:
@@ -2042,8 +2084,8 @@ __device__ void prefill_tile_bf16(const MainArgs& a, int h, int tile, int q0, in
       const uint32_t ok_ = in ? base + static_cast<uint32_t>(lpos ^ kswz<D>(row)) * 16 : kOffsetOutOfRange;
       const uint32_t ov_ = in ? base + static_cast<uint32_t>(lpos ^ vswz<D>(row)) * 16 : kOffsetOutOfRange;
       unsigned char* dk = st + (KPW * w + RPI * j) * ROW;
-      load_lds16(rk, dk, ok_);
-      load_lds16(rv, dk + POOL, ov_);
+      load_lds16_async(rk, dk, ok_);
+      load_lds16_async(rv, dk + POOL, ov_);
     }
   };
 
@@ -2102,7 +2144,7 @@ __device__ void prefill_tile_bf16(const MainArgs& a, int h, int tile, int q0, in
     float tmax = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sc[v]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));  // lanes l and l^32 hold one row: same decision
+    tmax = max_xor32(tmax);  // lanes l and l^32 hold one row: same decision
     const float m_old = m_run[r];
     const float m_new = fmaxf(m_old, tmax);
     const bool move = !(m_new * a.scale_log2 - m_old * a.scale_log2 <= 8.f);  // also from -inf
@@ -2188,7 +2230,7 @@ __device__ void prefill_tile_bf16(const MainArgs& a, int h, int tile, int q0, in
   issue_step(2 * BN, page_ref(2 * BN), st2);
   PageRef nref = page_ref(3 * BN);
   __builtin_amdgcn_s_waitcnt(kWaitTwoSteps);  // step 0 landed
-  __syncthreads();
+  stage_barrier();
   f32x16_t sa, sb;  // S of the next half step, row blocks 0 and 1
   u32x4_t p0[2], p1[2];
   u32x4_t kf[KS];     // K operands of the next half step
@@ -2202,7 +2244,7 @@ __device__ void prefill_tile_bf16(const MainArgs& a, int h, int tile, int q0, in
   rescale(0, softmax(sa, 0, p0));
   load_k(st0, 1, kf);
   __builtin_amdgcn_s_waitcnt(kWaitOneStep);  // step 1 landed
-  __syncthreads();
+  stage_barrier();
 
   // unit h = 2 j + kb (cur holds step j, nxt step j + 1).  Operand reads run
   // one region ahead: region 1 reads V(h) for region 2, region 2 reads
@@ -2246,7 +2288,7 @@ __device__ void prefill_tile_bf16(const MainArgs& a, int h, int tile, int q0, in
     // step j + 2 has landed (j + 3 may still stream); after the barrier every
     // wave's has, and stage j is free
     __builtin_amdgcn_s_waitcnt(kWaitOneStep);
-    __syncthreads();
+    stage_barrier();
   };
   // four steps per trip, so that each step's stages are fixed objects
   for (int j = 0; j < nsteps; j += 4) {
@@ -2261,7 +2303,7 @@ __device__ void prefill_tile_bf16(const MainArgs& a, int h, int tile, int q0, in
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
     const int my_row = wrow0 + 32 * r + qc;
-    const float l_tot = l_run[r] + __shfl_xor(l_run[r], 32);  // lanes l and l^32 share a row
+    const float l_tot = sum_xor32(l_run[r]);  // lanes l and l^32 share a row
     if (my_row >= Lq) continue;
     const float inv = 1.f / l_tot;
     bf16_t* op = static_cast<bf16_t*>(a.out) + (static_cast<size_t>(q0 + my_row) * a.num_heads + h) * D;
@@ -2295,6 +2337,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs p) {
   if (tile * kPrefillRows >= lq) return;
   prefill_tile_bf16<D, kContig>(p.m, h, tile, q0, lq, lk, st0, st1, st2, st3);
 }
+
 
 // ==================================================================== launch
 namespace {
