@@ -464,6 +464,17 @@ struct MainArgs {
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// Lanes l and l ^ 32 combined with one VALU lane swap (v_permlane32_swap)
+// instead of an LDS permute, whose result would wait behind every LDS read
+// issued before it.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Position of the largest entry of the non-decreasing prefix[0..n] that is
 // <= x, i.e. the segment owning item x.
@@ -1931,17 +1942,6 @@ __device__ __forceinline__ void load_lds16_async(__amdgpu_buffer_rsrc_t rsrc, un
   const auto lp = (__attribute__((address_space(3))) unsigned char*)dst;
   const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lp)));
   asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(off), "s"(rsrc), "{m0}"(lds) : "memory");
-}
-// Lanes l and l ^ 32 combined with one VALU lane swap (v_permlane32_swap)
-// instead of an LDS permute, whose result would wait behind every LDS read
-// issued before it.
-__device__ __forceinline__ float max_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 // Workgroup barrier that leaves the pool-to-LDS loads in flight.  A
 // __syncthreads() fences LDS at workgroup scope, and since those loads write
