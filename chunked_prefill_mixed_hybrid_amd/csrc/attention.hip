@@ -2140,6 +2140,10 @@ __device__ void prefill_tile_bf16(const MainArgs& a, int h, int tile, int q0, in
   // reference), so the accumulator rescale -- 64 multiplies per row block,
   // behind a branch -- is left for the rare large jumps instead of every new
   // maximum (on N(0,1) data a wave saw one in about three half steps).
+  // whether any row of a block moved its reference max in the last softmax:
+  // a wave-wide vote taken right after the max, so the rescale branch does not
+  // wait for the exponential that gives the factor
+  bool moved[RB] = {};
   auto softmax = [&](const f32x16_t& sc, int r, u32x4_t (&pk)[2]) -> float {
     float tmax = -INFINITY;
 #pragma unroll
@@ -2148,6 +2152,7 @@ __device__ void prefill_tile_bf16(const MainArgs& a, int h, int tile, int q0, in
     const float m_old = m_run[r];
     const float m_new = fmaxf(m_old, tmax);
     const bool move = !(m_new * a.scale_log2 - m_old * a.scale_log2 <= 8.f);  // also from -inf
+    moved[r] = __any(move);
     const float m_ref = move ? m_new : m_old;
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
     const float alpha = move ? fast_exp2((m_old - m_use) * a.scale_log2) : 1.f;
@@ -2169,7 +2174,7 @@ __device__ void prefill_tile_bf16(const MainArgs& a, int h, int tile, int q0, in
     return alpha;
   };
   auto rescale = [&](int r, float alpha) {
-    if (__any(alpha != 1.f)) {  // no row max moved: the accumulators need no rescale
+    if (moved[r]) {  // no row max moved: the accumulators need no rescale
 #pragma unroll
       for (int m = 0; m < NM; ++m) acc[r][m] *= alpha;
     }
