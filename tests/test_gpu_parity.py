@@ -81,6 +81,45 @@ def _dev(hs):
     return W.to_device(hs, "cuda")
 
 
+# ---------------------------------------------------------------- random steps
+# Seeded random mixed steps through hybrid_step_fwd: 1-40 segments -- decodes
+# (history 1..6000), at most 3 chunks (2..700 rows at history 0..3000) and
+# empty segments -- 1-8 KV heads in GQA groups of 1, 2 or 4, D 64 or 128, bf16
+# or fp32.  Pools bit-exact, the whole output within the oracle's tolerance.
+def _random_step(case):
+    rng = np.random.default_rng(7000 + case)
+    segs, chunks = [], 0
+    for _ in range(int(rng.integers(1, 41))):
+        u = rng.random()
+        if u < 0.3 and chunks < 3:
+            chunks += 1
+            lq = int(rng.integers(2, 701))
+            segs.append((lq, lq + int(rng.integers(0, 3001))))
+        elif u < 0.93:
+            segs.append((1, int(rng.integers(1, 6001))))
+        else:
+            segs.append((0, int(rng.integers(0, 41))))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    d = int(rng.choice([64, 128]))
+    dt = W.F32 if rng.random() < 0.3 else W.BF16
+    return segs, hq, hkv, d, dt
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_random_step(case):
+    segs, hq, hkv, d, dt = _random_step(case)
+    spec, meta = W.custom_step(segs, hq, hkv, d, dt, seed=7000 + case)
+    hs = W.host_values(spec, meta, seed=7000 + case)
+    ds = _dev(hs)
+    ref, kc_ref, vc_ref = G.oracle_full(ds, hs.k_cache, hs.v_cache)
+    G.note(f"random step {case}: {len(segs)} segments, total_q {meta.total_q}, H={hq}/{hkv} D={d} {dt}")
+    out = _step(ds, None)
+    kc, vc = G.host_pools(ds)
+    assert kc.tobytes() == kc_ref.tobytes() and vc.tobytes() == vc_ref.tobytes()
+    G.compare(G.to_f64(out), ref, dt, f"random step {case}")
+
+
 # ---------------------------------------------------------------- chunk KV splits
 # Few, long chunk tiles and little decode work: the planner cuts every chunk
 # tile into key ranges whose partial results the last range to finish merges.
