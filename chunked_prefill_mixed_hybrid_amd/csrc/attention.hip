@@ -1937,11 +1937,17 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(MainArgs a) {
 // compiler does not see it write LDS: with dozens of these in flight its alias
 // tracking of such loads runs out of slots, and it then waits for all of them
 // in front of LDS reads of other stages.  The caller waits (vmcnt) for the
-// loads it needs; the instruction has no register result.
+// loads it needs; the instruction has no register result.  An LDS-DMA load
+// needs one wait state after the SALU write of M0 that it reads, which the
+// compiler inserts for its own such loads but cannot see here: hence the
+// s_nop.  (A VALU write of one of its SGPR operands needs five; the compiler
+// builds the descriptor and M0 with SALU instructions, and a kernel-structure
+// test checks both distances in the compiled code.)
 __device__ __forceinline__ void load_lds16_async(__amdgpu_buffer_rsrc_t rsrc, unsigned char* dst, uint32_t off) {
   const auto lp = (__attribute__((address_space(3))) unsigned char*)dst;
   const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lp)));
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(off), "s"(rsrc), "{m0}"(lds) : "memory");
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(off), "s"(rsrc), "{m0}"(lds)
+               : "memory");
 }
 // Workgroup barrier that leaves the pool-to-LDS loads in flight.  A
 // __syncthreads() fences LDS at workgroup scope, and since those loads write

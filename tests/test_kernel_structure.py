@@ -131,3 +131,77 @@ __global__ void probe(int* q, int* out, int n) {
     asm = _device_asm(src, tmp_path)
     funcs = _functions(asm)
     assert any(divergent_barrier_loops(lines) for lines in funcs.values())
+
+
+# ---------------------------------------------------------------- LDS-DMA wait states
+# A pool-to-LDS load (buffer_load ... lds) reads M0 (its LDS address) and the
+# buffer descriptor in SGPRs.  On gfx9-family chips it needs one wait state
+# after an SALU write of M0, and five after a VALU write of any SGPR it reads.
+# The compiler inserts them for the loads it emits itself; for loads written
+# as inline asm it cannot, so the compiled code is checked here.
+_SGPR = re.compile(r"^s\[(\d+):(\d+)\]$|^s(\d+)$")
+
+
+def _sgprs(tok):
+    tok = tok.strip(",")
+    if tok == "m0":
+        return {"m0"}
+    m = _SGPR.match(tok)
+    if not m:
+        return set()
+    if m.group(3) is not None:
+        return {int(m.group(3))}
+    return set(range(int(m.group(1)), int(m.group(2)) + 1))
+
+
+def lds_dma_hazards(lines: list) -> list:
+    """(load, writer, wait states) for every LDS-DMA load that follows an SALU
+    write of M0 by fewer than 1 wait state, or a VALU write of one of its SGPR
+    operands by fewer than 5, in one function's assembly."""
+    code = [l.strip() for l in lines]
+    code = [l for l in code if l and not l.startswith((";", ".")) and not l.endswith(":")]
+    found = []
+    for i, line in enumerate(code):
+        op = line.split()[0]
+        if not (op.startswith("buffer_load") and line.endswith(" lds")):
+            continue
+        reads = {"m0"}
+        for tok in line.split()[1:]:
+            reads |= _sgprs(tok)
+        waits = 0
+        for k in range(i - 1, max(i - 12, -1), -1):
+            prev = code[k].split()
+            dst = _sgprs(prev[1]) if len(prev) > 1 else set()
+            if prev[0].startswith("s_") and "m0" in dst and waits < 1:
+                found.append((line, code[k], waits))
+            if prev[0].startswith("v_") and dst & reads and waits < 5:
+                found.append((line, code[k], waits))
+            waits += int(prev[1]) + 1 if prev[0] == "s_nop" else 1
+            if waits >= 5:
+                break
+    return found
+
+
+@pytest.mark.parametrize("source", build.SOURCES)
+def test_lds_dma_wait_states(source, tmp_path):
+    asm = _device_asm(build.CSRC / source, tmp_path)
+    bad = {fn: f for fn, lines in _functions(asm).items() if (f := lds_dma_hazards(lines))}
+    assert not bad, f"LDS-DMA load too close to a write of its SGPR operands: {bad}"
+
+
+def test_lds_dma_detector_flags_a_missing_wait_state(tmp_path):
+    """The detector itself: an inline-asm LDS-DMA load right after the SALU
+    write of M0 (the compiler sees no load there) is flagged."""
+    src = tmp_path / "probe_dma.hip"
+    src.write_text(r"""
+#include <hip/hip_runtime.h>
+__global__ void probe_dma(const unsigned* src, int n) {
+  __shared__ __attribute__((aligned(16))) unsigned char st[4096];
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, n * 4, 0x00020000);
+  const auto lp = (__attribute__((address_space(3))) unsigned char*)(st + (threadIdx.x >> 6) * 1024);
+  const unsigned lds = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(reinterpret_cast<uintptr_t>(lp)));
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(threadIdx.x * 16), "s"(rs), "{m0}"(lds) : "memory");
+}
+""")
+    asm = _device_asm(src, tmp_path)
+    assert any(lds_dma_hazards(lines) for lines in _functions(asm).values())
