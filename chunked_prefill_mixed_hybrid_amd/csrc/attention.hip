@@ -2011,7 +2011,7 @@ __device__ void prefill_tile_bf16(const MainArgs& a, int h, int tile, int q0, in
                                   unsigned char* st0, unsigned char* st1, unsigned char* st2,
                                   unsigned char* st3) {
   using Cfg = ChunkCfg<bf16_t>::Sizes<D>;
-  constexpr int BN = Cfg::BN, NKB = BN / 32, KS = D / 16, NM = D / 32, RB = kPrefillBlocks;
+  constexpr int BN = Cfg::BN, KS = D / 16, NM = D / 32, RB = kPrefillBlocks;
   static_assert(RB == 2, "the pipeline below pairs the two row blocks");
   constexpr int ROW = Cfg::ROW, POOL = Cfg::POOL;
   constexpr int CPR = D / 8;          // 16-byte chunks per key row
@@ -2146,38 +2146,65 @@ __device__ void prefill_tile_bf16(const MainArgs& a, int h, int tile, int q0, in
   // reference), so the accumulator rescale -- 64 multiplies per row block,
   // behind a branch -- is left for the rare large jumps instead of every new
   // maximum (on N(0,1) data a wave saw one in about three half steps).
-  // whether any row of a block moved its reference max in the last softmax:
-  // a wave-wide vote taken right after the max, so the rescale branch does not
-  // wait for the exponential that gives the factor
+  // moved[r]: whether any row of block r moved its reference max in the last
+  // softmax, a wave-wide vote taken right after the max, so the rescale
+  // branch does not wait for the exponential that gives the factor.
+  // The softmax is cut into kSmPieces pieces -- 4 of the row max, the
+  // reference decision, 8 pairs of weights, the running sum -- so that one
+  // region can spread it between its MFMAs in source order (qk_softmax).
   bool moved[RB] = {};
-  auto softmax = [&](const f32x16_t& sc, int r, u32x4_t (&pk)[2]) -> float {
-    float tmax = -INFINITY;
+  struct SmState { float tmax, alpha, neg_m, psum; };
+  constexpr int kSmPieces = 14;
+  auto sm_piece = [&](int i, const f32x16_t& sc, int r, u32x4_t (&pk)[2], SmState& st) {
+    if (i < 4) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sc[v]);
-    tmax = max_xor32(tmax);  // lanes l and l^32 hold one row: same decision
-    const float m_old = m_run[r];
-    const float m_new = fmaxf(m_old, tmax);
-    const bool move = !(m_new * a.scale_log2 - m_old * a.scale_log2 <= 8.f);  // also from -inf
-    moved[r] = __any(move);
-    const float m_ref = move ? m_new : m_old;
-    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    const float alpha = move ? fast_exp2((m_old - m_use) * a.scale_log2) : 1.f;
-    const float neg_m = -m_use * a.scale_log2;
-    m_run[r] = m_ref;
-    float psum = 0.f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const float p0 = fast_exp2(fmaf(sc[8 * u + 2 * e2], a.scale_log2, neg_m));
-        const float p1 = fast_exp2(fmaf(sc[8 * u + 2 * e2 + 1], a.scale_log2, neg_m));
-        const uint32_t w2 = pack_bf16x2(p0, p1);
-        pk[u][e2] = w2;
-        psum = dot2_bf16(w2, kBf16PairOne, psum);  // the same rounded weights P.V uses
-      }
+      for (int v = 4 * i; v < 4 * i + 4; ++v) st.tmax = fmaxf(st.tmax, sc[v]);
+    } else if (i == 4) {
+      const float tmax = max_xor32(st.tmax);  // lanes l and l^32 hold one row: same decision
+      const float m_old = m_run[r];
+      const float m_new = fmaxf(m_old, tmax);
+      const bool move = !(m_new * a.scale_log2 - m_old * a.scale_log2 <= 8.f);  // also from -inf
+      moved[r] = __any(move);
+      const float m_ref = move ? m_new : m_old;
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      st.alpha = move ? fast_exp2((m_old - m_use) * a.scale_log2) : 1.f;
+      st.neg_m = -m_use * a.scale_log2;
+      m_run[r] = m_ref;
+    } else if (i < 13) {
+      const int e = i - 5;  // weights of values 2e, 2e + 1
+      const float p0 = fast_exp2(fmaf(sc[2 * e], a.scale_log2, st.neg_m));
+      const float p1 = fast_exp2(fmaf(sc[2 * e + 1], a.scale_log2, st.neg_m));
+      const uint32_t w2 = pack_bf16x2(p0, p1);
+      pk[e >> 2][e & 3] = w2;
+      st.psum = dot2_bf16(w2, kBf16PairOne, st.psum);  // the same rounded weights P.V uses
+    } else {
+      l_run[r] = l_run[r] * st.alpha + st.psum;
     }
-    l_run[r] = l_run[r] * alpha + psum;
-    return alpha;
+  };
+  auto softmax = [&](const f32x16_t& sc, int r, u32x4_t (&pk)[2]) -> float {
+    SmState st{-INFINITY, 1.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kSmPieces; ++j) sm_piece(j, sc, r, pk, st);
+    return st.alpha;
+  };
+  // S = K Q^T of the next key block (both row blocks, MFMAs alternating
+  // between them) with the softmax of row block r of the current block spread
+  // between the MFMAs.  Written out in this order because the compiler's
+  // scheduler, asked to interleave the two (as for the P.V region below),
+  // put the whole softmax after the last MFMA at D = 128, where registers
+  // are tightest.
+  auto qk_softmax = [&](const u32x4_t (&kf)[KS], f32x16_t& s0, f32x16_t& s1, const f32x16_t& sc, int r,
+                        u32x4_t (&pk)[2]) -> float {
+    SmState st{-INFINITY, 1.f, 0.f, 0.f};
+    s0 = s1 = f32x16_t{};
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      if (i & 1) s1 = mfma_bf16(kf[i >> 1], qf[1][i >> 1], s1);
+      else s0 = mfma_bf16(kf[i >> 1], qf[0][i >> 1], s0);
+#pragma unroll
+      for (int j = i * kSmPieces / (2 * KS); j < (i + 1) * kSmPieces / (2 * KS); ++j) sm_piece(j, sc, r, pk, st);
+    }
+    return st.alpha;
   };
   auto rescale = [&](int r, float alpha) {
     if (moved[r]) {  // no row max moved: the accumulators need no rescale
@@ -2269,9 +2296,7 @@ __device__ void prefill_tile_bf16(const MainArgs& a, int h, int tile, int q0, in
   auto unit = [&](int h, const unsigned char* cur, const unsigned char* nxt, int kb) {
     const f32x16_t sc = sb;  // S of half step h, row block 1
     load_v(cur + POOL, kb, vf);
-    qk(kf, sa, sb);
-    float alpha1 = softmax(sc, 1, p1);
-    interleave(std::integral_constant<int, 4 * NM>{});
+    float alpha1 = qk_softmax(kf, sa, sb, sc, 1, p1);
     pin(p1, alpha1);
     const int kn = (h + 1) * 32;  // first key of half step h + 1
     if (kn + 31 > H0 + wrow0) {
