@@ -2027,8 +2027,14 @@ __device__ void prefill_tile_bf16(const MainArgs& a, int h, int tile, int q0, in
   const int qc = lane & 31, g = lane >> 5;
   const int H0 = Lk - Lq;
   const int kvh = h / a.group;
-  const int row0 = tile * kPrefillRows;
-  const int rows_end = min(row0 + kPrefillRows, Lq);
+  // Tiles are aligned to the chunk's end: tile t holds rows
+  // [256 t - shift, 256 (t + 1) - shift) with shift = 256 ceil(Lq / 256) - Lq,
+  // so the one partial tile is the first, which sees the fewest keys (every
+  // wave runs every step of its tile, rows or not).  Rows below 0 are masked
+  // out like rows past a wave's diagonal and are never stored.
+  const int shift = (Lq + kPrefillRows - 1) / kPrefillRows * kPrefillRows - Lq;
+  const int row0 = tile * kPrefillRows - shift;
+  const int rows_end = row0 + kPrefillRows;
   const int kb1 = H0 + rows_end;  // keys [0, kb1) are visible to some row of the tile
   const int nsteps = (kb1 + BN - 1) / BN;
   const int wrow0 = row0 + w * 32 * RB;
@@ -2039,7 +2045,7 @@ __device__ void prefill_tile_bf16(const MainArgs& a, int h, int tile, int q0, in
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
     const int row = wrow0 + 32 * r + qc;
-    const bool ok = row < Lq;
+    const bool ok = row >= 0 && row < Lq;
     const bf16_t* qp = static_cast<const bf16_t*>(a.q) +
                        (static_cast<size_t>(q0 + (ok ? row : 0)) * a.num_heads + h) * D + g * 8;
 #pragma unroll
@@ -2340,7 +2346,7 @@ __device__ void prefill_tile_bf16(const MainArgs& a, int h, int tile, int q0, in
   for (int r = 0; r < RB; ++r) {
     const int my_row = wrow0 + 32 * r + qc;
     const float l_tot = sum_xor32(l_run[r]);  // lanes l and l^32 share a row
-    if (my_row >= Lq) continue;
+    if (my_row < 0 || my_row >= Lq) continue;
     const float inv = 1.f / l_tot;
     bf16_t* op = static_cast<bf16_t*>(a.out) + (static_cast<size_t>(q0 + my_row) * a.num_heads + h) * D;
 #pragma unroll
@@ -2356,7 +2362,7 @@ __device__ void prefill_tile_bf16(const MainArgs& a, int h, int tile, int q0, in
 }
 
 // One workgroup per (tile, head), tiles with the most keys first (the last
-// tiles of a causal chunk); with Hq a multiple of 8 the tiles of one head all
+// tiles of a causal chunk, which are all whole); with Hq a multiple of 8 the tiles of one head all
 // run on one XCD (workgroups go to XCDs round robin), sharing its L2.
 template <int D, bool kContig>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs p) {

@@ -173,6 +173,8 @@ PREFILL_CASES = [
     ([(300, 300)], 128, 128, 64, W.BF16, 43),
     ([(513, 530)], 128, 128, 128, W.BF16, 44),    # one row in the last tile, history 17
     ([(1000, 1000)], 32, 32, 128, W.BF16, 45),    # 4 x 32 pairs: below one per CU, fused path
+    ([(1024, 1500)], 64, 16, 128, W.BF16, 46),    # whole tiles only, GQA 4
+    ([(200, 700)], 256, 32, 64, W.BF16, 47),      # one partial tile per head, GQA 8
 ]
 _SENTINEL = 0x5A
 
