@@ -2249,14 +2249,14 @@ __device__ void prefill_tile_bf16(const MainArgs& a, int h, int tile, int q0, in
         acc[1][m] = mfma_bf16(vf[m][u], p1[u], acc[1][m]);
       }
   };
-  // order of a region: its 16 MFMAs, each followed by a share of the LDS
-  // reads (operands of the next region) and of the VALU work
-  auto interleave = [&](auto reads) {
-    constexpr int R = decltype(reads)::value / (2 * KS);
+  // order of the P.V region: its 2 KS MFMAs, each followed by up to five VALU
+  // instructions of the softmax that runs under them (the region's K operand
+  // reads are left where the compiler puts them)
+  auto interleave = [&]() {
 #pragma unroll
     for (int i = 0; i < 2 * KS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x100, 0, 0);  // no LDS read
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
     }
   };
@@ -2314,7 +2314,7 @@ __device__ void prefill_tile_bf16(const MainArgs& a, int h, int tile, int q0, in
     load_k(nxt, kb, kf);
     pv(vf, p0, p1);
     float alpha0 = softmax(sa, 0, pn);
-    interleave(std::integral_constant<int, KS>{});
+    interleave();
     pin(pn, alpha0);
     rescale(0, alpha0);
     p0[0] = pn[0];
