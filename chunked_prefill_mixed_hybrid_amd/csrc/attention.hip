@@ -2030,8 +2030,9 @@ __device__ void prefill_tile_bf16(const MainArgs& a, int h, int tile, int q0, in
   // Tiles are aligned to the chunk's end: tile t holds rows
   // [256 t - shift, 256 (t + 1) - shift) with shift = 256 ceil(Lq / 256) - Lq,
   // so the one partial tile is the first, which sees the fewest keys (every
-  // wave runs every step of its tile, rows or not).  Rows below 0 are masked
-  // out like rows past a wave's diagonal and are never stored.
+  // wave runs every step of its tile, rows or not).  Rows below 0 take zero
+  // queries and the keys the causal rule gives them (none without history);
+  // they are never stored.
   const int shift = (Lq + kPrefillRows - 1) / kPrefillRows * kPrefillRows - Lq;
   const int row0 = tile * kPrefillRows - shift;
   const int rows_end = row0 + kPrefillRows;
