@@ -120,6 +120,36 @@ def test_random_step(case):
     G.compare(G.to_f64(out), ref, dt, f"random step {case}")
 
 
+def _random_prefill(case):
+    """A seeded one-segment bf16 step with at least one (256-row tile, head)
+    pair per CU of a 256-CU device, so that it takes the one-segment prefill
+    kernel: Lq spread over partial-tile sizes, with or without history."""
+    rng = np.random.default_rng(7500 + case)
+    hq = int(rng.choice([64, 128]))
+    hkv = hq // int(rng.choice([1, 2, 4, 8]))
+    lq = int(rng.integers(256 * (256 // hq - 1) + 1, 1400))
+    h0 = 0 if rng.random() < 0.4 else int(rng.integers(1, 1500))
+    return [(lq, lq + h0)], hq, hkv, int(rng.choice([64, 128]))
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_one_segment_prefill(case):
+    """Random one-segment prefills through hybrid_step_fwd: the first tile's
+    missing rows (256 ceil(Lq / 256) - Lq of them) vary from case to case."""
+    segs, hq, hkv, d = _random_prefill(case)
+    spec, meta = W.custom_step(segs, hq, hkv, d, W.BF16, seed=7500 + case)
+    hs = W.host_values(spec, meta, seed=7500 + case)
+    ds = _dev(hs)
+    ref, kc_ref, vc_ref = G.oracle_full(ds, hs.k_cache, hs.v_cache)
+    lq = segs[0][0]
+    G.note(f"random one-segment prefill {case}: segs={segs} H={hq}/{hkv} D={d} "
+           f"missing rows {(lq + 255) // 256 * 256 - lq} prefill kernel={_prefill_expected(meta, hq, W.BF16)}")
+    out = _step(ds, None)
+    kc, vc = G.host_pools(ds)
+    assert kc.tobytes() == kc_ref.tobytes() and vc.tobytes() == vc_ref.tobytes()
+    G.compare(G.to_f64(out), ref, W.BF16, f"random one-segment prefill {case}")
+
+
 # ---------------------------------------------------------------- chunk KV splits
 # Few, long chunk tiles and little decode work: the planner cuts every chunk
 # tile into key ranges whose partial results the last range to finish merges.
